@@ -1,0 +1,684 @@
+// bf16 kernels for gfx950 (CDNA4): W_UK absorption, sparse latent attention,
+// split merge + W_UV absorption.  All matrix products run on bf16 MFMA with
+// float32 accumulation.
+//
+// MFMA operand layouts used below (64-lane wavefront, l = lane id):
+//   v_mfma_f32_16x16x32_bf16: A[m][k] from lane (m + 16*(k/8)), element k%8;
+//     B[k][n] from lane (n + 16*(k/8)), element k%8; D[m][n] in lane
+//     (n + 16*(m/4)), element m%4.
+//   v_mfma_f32_32x32x16_bf16: A[m][k] from lane (m + 32*(k/8)), element k%8;
+//     B[k][n] from lane (n + 32*(k/8)), element k%8; D[m][n] in lane
+//     (n + 32*((m/4)%2)), element 4*(m/8) + m%4.
+// Any permutation of k applied to both operands leaves the product unchanged;
+// the attention kernel uses that to match the transposing LDS read below.
+//
+// ds_read_b64_tr_b16 (transposing LDS read): within each 16-lane block, lane
+// i receives element e (e = 0..3) from the 8-byte chunk addressed by lane
+// 4e + i/4, element i%4.  If lane 4e + q of a block addresses row r_e,
+// columns c + 4q .. c + 4q + 3 of a row-major bf16 matrix, lane i of the
+// block receives column c + i of rows r_0 .. r_3: a column-major MFMA operand
+// read from row-major storage.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    bf16x4 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    r[2] = (__bf16)c;
+    r[3] = (__bf16)d;
+    return r;
+}
+
+// Score-chain MFMAs with the accumulator in ordinary VGPRs.  The mix
+// accumulator takes all 256 accumulation registers, so the compiler (which
+// picks one MFMA register form per kernel) would otherwise shuttle the score
+// tile through them.  Chained MFMAs that read the previous result as their
+// accumulator input (exact overlap) need no wait states; mfma_settle covers
+// the MFMA-write -> VALU-read window before the scores are read.
+__device__ __forceinline__ void mfma32_v_first(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle(f32x16& d) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+
+// Transposing read of four bf16 (see the header comment).
+__device__ __forceinline__ bf16x4 lds_read_tr(const lds_u8* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Buffer resource over `bytes` bytes at `base`.  A raw buffer load whose
+// offset is >= bytes returns zeros without touching memory; kOutOfRange is
+// such an offset for every buffer these kernels build (<= 2 GiB).
+constexpr unsigned kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// --------------------------------------------------------------------------
+// Step 1: q_c[r, h, :] = q_nope[r, h, :] . W_UK[h]  (and append q_pe)
+//
+// Per head this is a [R x 128] . [128 x 512] product, computed transposed,
+// q_c^T = W_UK[h]^T . q_nope^T: the weight is the A operand (its columns c
+// become MFMA rows) and each lane's output holds four consecutive c of one
+// query row.  Workgroup = (head, quarter of c, group of 32-row query blocks).
+// The weight slice [128 d x 128 c] is staged in LDS with 16-byte loads and
+// read back transposed; wave w keeps the fragments of its 32 columns in
+// registers for every query block it visits.
+// --------------------------------------------------------------------------
+constexpr int kWRow = 320;   // bytes per staged W_UK row (128 bf16 + pad)
+
+__global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ q_nope,
+                                                     const __bf16* __restrict__ q_pe,
+                                                     const __bf16* __restrict__ w_uk,
+                                                     __bf16* __restrict__ q_out, int R,
+                                                     int r_groups) {
+    __shared__ __attribute__((aligned(16))) unsigned char wbuf[kNope * kWRow];
+    const int h = blockIdx.x >> 2;
+    const int cq = blockIdx.x & 3;
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+
+    {
+        // 128 rows d x 16 chunks of 8 columns; 8 chunks per thread
+        const __bf16* src = w_uk + (size_t)h * kNope * kLatent + cq * 128;
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(e >> 4) * kLatent + 8 * (e & 15));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            *reinterpret_cast<u32x4*>(wbuf + (e >> 4) * kWRow + 16 * (e & 15)) = v[i];
+        }
+    }
+    __syncthreads();
+
+    // A fragments: W_UK[h][d][c] for c = 32*wave + lane%32 (within the quarter),
+    // d = 16*ks + 8*half + e (e = 0..7) via two transposing reads.
+    bf16x8 a[8];
+    {
+        const int blk = lane >> 4, e4 = (lane & 15) >> 2, q = lane & 3;
+        const lds_u8* base = (const lds_u8*)wbuf + (8 * (blk >> 1) + e4) * kWRow +
+                             (32 * wave + 16 * (blk & 1) + 4 * q) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            a[ks] = cat(lds_read_tr(base + 16 * ks * kWRow), lds_read_tr(base + (16 * ks + 4) * kWRow));
+    }
+
+    const int c_base = cq * 128 + wave * 32;
+    for (int rb = blockIdx.y; rb * 32 < R; rb += r_groups) {
+        const int r = rb * 32 + (lane & 31);
+        const bool rv = r < R;
+        f32x16 acc = {};
+        const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 8 * half;
+        bf16x8 b[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) b[ks] = rv ? *reinterpret_cast<const bf16x8*>(qn + 16 * ks) : bf16x8{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], b[ks], acc);
+        if (rv) {
+            __bf16* dst = q_out + ((size_t)r * kHeads + h) * kQRow + c_base + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
+                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+        if (cq == 0) {
+            // q_pe rows of this block: 32 rows x 8 chunks of 16 bytes = one per thread.
+            const int rr = rb * 32 + (threadIdx.x >> 3);
+            const int ch = threadIdx.x & 7;
+            if (rr < R) {
+                *reinterpret_cast<bf16x8*>(q_out + ((size_t)rr * kHeads + h) * kQRow + kLatent + 8 * ch) =
+                    *reinterpret_cast<const bf16x8*>(q_pe + ((size_t)rr * kHeads + h) * kRope + 8 * ch);
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Steps 2-4: sparse attention over the selected latent rows.
+//
+// Workgroup = (query row r, split of its index list): four waves, wave w owns
+// heads 32w .. 32w+31 and every selected row of the split, so no wave waits on
+// another except to share the row tiles.  Selected rows are gathered 32 at a
+// time straight into LDS (buffer loads with an LDS destination, so the data
+// never occupies registers) through four tile buffers: three tiles are in
+// flight while one is consumed, and one barrier per tile hands a buffer from
+// readers to the next gather.  Per tile and wave:
+//   scores   S^T[j][h] = sum_c row_j[c] Q[h][c] (v_mfma 32x32x16, Q in
+//            registers as the B operand); each lane ends up owning one head h
+//            and sixteen rows j;
+//   softmax  per lane, in the log2 domain, against a reference m taken from
+//            the head's first tile with a selected row: p = 2^(s - m).  The
+//            accumulator is never rescaled (which keeps it in the accumulation
+//            registers); if any later score beats m by more than 32, which no
+//            realistic attention does, a fallback recomputes the split with
+//            the exact per-head maxima;
+//   mix      O~^T[c][h] += sum_j V^T[c][j] P^T[j][h] (v_mfma 32x32x16).  The
+//            score accumulator already holds P^T in the B-operand layout of the
+//            mix, provided MFMA k slot 4t + e of lane half g is row
+//            16kc + 8t + 4g + e; V^T comes from the row-major tile through the
+//            transposing LDS read with the same slot order.
+// LDS tile layout: latent rows at 1024-byte stride with 16-byte chunk q of
+// row j stored at chunk q ^ swz(j); rotary rows in four 8-row blocks (1152-byte
+// stride) with chunk c of block row j' at c ^ j'.  Both the score reads and the
+// transposing reads then touch each bank once per pass.
+// Empty or out-of-range slots load with an out-of-range buffer offset (no
+// memory access) and are masked to -inf before the softmax.
+// --------------------------------------------------------------------------
+constexpr int kRows = kTileRows;             // rows per tile
+constexpr int kBufs = 4;                     // tile buffers
+constexpr int kLatBytes = kRows * 1024;
+constexpr int kPeBlock = 1152;               // 8 rotary rows (1 KiB) + 128-byte pad
+constexpr int kBufBytes = kLatBytes + 4 * kPeBlock;
+
+__device__ __forceinline__ int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+#define MLA_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// 16-byte-per-lane buffer load straight into LDS: lane l's 16 bytes land at
+// LDS byte address lds_addr + 16*l (lds_addr must be wave-uniform); an offset
+// past the buffer's size reads zeros.  Written as inline assembly so that the
+// compiler does not order the kernel's LDS reads behind every gather in flight
+// (it cannot tell the tile buffers apart); the kernel orders them itself with
+// explicit vmcnt waits and barriers.  No register receives data, and M0 is
+// restored before the block ends.
+__device__ __forceinline__ void load_lds16(u32x4 rsrc, unsigned lds_addr, unsigned voff) {
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
+// Raw buffer descriptor (stride 0) over `bytes` bytes at `base`.
+__device__ __forceinline__ u32x4 make_desc(const void* base, unsigned bytes) {
+    const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+    return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// Everything one workgroup needs to process one (query row, split).
+struct SplitCtx {
+    const AttnArgs* a;
+    unsigned char* tiles;        // kBufs tile buffers in LDS (generic pointer to LDS)
+    const int* sidx;             // the split's index list in LDS (-1 past its end)
+    const __bf16* qrow;          // this lane's absorbed-query row, offset to its k half
+    u32x4 kv_desc, pe_desc;
+    int r, split, ntiles, limit, T, wave, lane;
+};
+
+// Gather tile t into buffer t % kBufs: wave w fetches rows 8w .. 8w+7 (eight
+// 1 KiB latent rows, then one instruction for their rotary parts).  Empty or
+// out-of-range slots use an out-of-range offset: no memory is touched.
+__device__ __forceinline__ void gather_tile(const SplitCtx& c, int t) {
+    unsigned char* buf = c.tiles + (t & (kBufs - 1)) * kBufBytes;
+    // Opaque copy of the lane id: keeps the per-row lane offsets from being
+    // hoisted out of the tile loop (they would pin eight registers).
+    int ln = c.lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 8 * c.wave + q;
+        const int p = c.sidx[t * kRows + row];
+        const bool ok = p >= 0 && p < c.T && p <= c.limit;
+        const unsigned off = ok ? (unsigned)p * 1024u + ((unsigned)(ln ^ lat_swz(row)) << 4) : kOutOfRange;
+        load_lds16(c.kv_desc, (unsigned)(size_t)(buf + row * 1024), off);
+    }
+    const int jp = ln >> 3;
+    const int p = c.sidx[t * kRows + 8 * c.wave + jp];
+    const bool ok = p >= 0 && p < c.T && p <= c.limit;
+    const unsigned off = ok ? (unsigned)p * 128u + ((unsigned)((ln & 7) ^ jp) << 4) : kOutOfRange;
+    load_lds16(c.pe_desc, (unsigned)(size_t)(buf + kLatBytes + c.wave * kPeBlock), off);
+}
+
+// One pass over the split's tiles: accumulate against a reference taken from
+// each head's first tile with a selected row; `beaten` reports a tile that
+// beat it by more than 32 (log2 units).
+__device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
+                                          float& l_run, bool& beaten) {
+    const int lane = c.lane;
+    const int ntiles = c.ntiles;
+    // Query fragments (B operands): head 32*wave + lane%32, columns
+    // 16*ks + 8*(lane/32) .. +7.  Retiring their loads here leaves vmcnt
+    // counting the gathers only inside the tile loop.
+    bf16x8 qf[36];
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 16 * ks);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // Per-lane LDS offsets, relative to a tile buffer.  Buffer offsets are
+    // multiples of 512 bytes, so XOR-ing a compile-time constant into bits 5..7
+    // of an offset commutes with adding the buffer offset.
+    const int j = lane & 31;            // score operand row
+    const int hsel = lane >> 5;         // which 8 of the MFMA's 16 k values
+    // latent chunk (2ks + hsel) of row j sits at ((2ks + hsel) ^ swz(j)):
+    // offset = sc_base ^ ((ks % 8) << 5), plus 256 bytes per 8 ks
+    const int sc_base = j * 1024 + ((hsel ^ lat_swz(j)) << 4);
+    // rotary chunk (2ks + hsel) of block row j%8 sits at ((2ks + hsel) ^ (j%8))
+    const int pe_base = kLatBytes + (j >> 3) * kPeBlock + (j & 7) * 128 + ((hsel ^ (j & 7)) << 4);
+    // transposing reads: 16-lane block blk reads rows 16kc + 8t + 4g + e4
+    // (g = blk/2, e4 = (lane%16)/4) and columns 32cb + 16(blk%2) + 4(lane%4):
+    // offset = tr_base[kc][t] ^ ((cb % 4) << 6), plus 256 bytes per 4 cb
+    const int blk = lane >> 4, g = blk >> 1, e4 = (lane & 15) >> 2, q4 = lane & 3;
+    const int lo = 2 * (blk & 1) + (q4 >> 1);
+    int tr_base[2][2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = 16 * kc + 8 * t + 4 * g + e4;   // lat_swz(row) = 4*e4 + 2t + g
+            tr_base[kc][t] = row * 1024 + (e4 << 6) + ((lo ^ (2 * t + g)) << 4) + (q4 & 1) * 8;
+        }
+
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
+    l_run = 0.f;
+    gather_tile(c, 0);
+    if (ntiles > 1) gather_tile(c, 1);
+    if (ntiles > 2) gather_tile(c, 2);
+
+    for (int t = 0; t < ntiles; ++t) {
+        // own gathers of tile t done (9 loads per tile; later tiles may stay in flight)
+        const int ahead = min(ntiles - 1 - t, 2);
+        if (ahead >= 2) MLA_WAIT_VMCNT(18);
+        else if (ahead == 1) MLA_WAIT_VMCNT(9);
+        else MLA_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();   // every wave's gathers of t landed; t-1 fully read
+        if (t + 3 < ntiles) gather_tile(c, t + 3);
+
+        const lds_u8* buf = (const lds_u8*)c.tiles + (t & (kBufs - 1)) * kBufBytes;
+        const int pv = c.sidx[t * kRows + j];
+        const unsigned vmask =
+            (unsigned)__builtin_amdgcn_ballot_w64(pv >= 0 && pv < c.T && pv <= c.limit);
+
+        // ---- scores S^T (rows x heads), accumulated in ordinary VGPRs
+        f32x16 sacc;
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+            const bf16x8 av = *(const __attribute__((address_space(3))) bf16x8*)(
+                buf + ((sc_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+            if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
+            else mfma32_v(sacc, av, qf[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 av =
+                *(const __attribute__((address_space(3))) bf16x8*)(buf + (pe_base ^ (ks << 5)));
+            mfma32_v(sacc, av, qf[32 + ks]);
+        }
+        mfma_settle(sacc);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 8 * (i >> 2) + 4 * hsel + (i & 3);
+            const bool ok = (vmask >> row) & 1u;
+            sacc[i] = ok ? sacc[i] * c.a->scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sacc[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (m_ref == -INFINITY) m_ref = mx;   // nothing accumulated for this head yet
+        else if (mx > m_ref + 32.f) beaten = true;
+
+        // ---- probabilities p = 2^(s - m_ref) <= 2^32, as bf16 B operands
+        bf16x8 pb[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = (sacc[i] == -INFINITY) ? 0.f : exp2f(sacc[i] - m_ref);
+            psum += p;
+            pb[i >> 3][i & 7] = (__bf16)p;
+        }
+        l_run += psum;
+
+        // ---- mix: O~^T[c][h] += V^T[c][j] P^T[j][h]
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
+                const bf16x8 av = cat(lds_read_tr(buf + ((tr_base[kc][0] ^ x) + y)),
+                                      lds_read_tr(buf + ((tr_base[kc][1] ^ x) + y)));
+                acc[cb] = mfma32(av, pb[kc], acc[cb]);
+            }
+        }
+    }
+    MLA_WAIT_VMCNT(0);
+}
+
+// Write this split's normalised bf16 mix (+ reference and sum when split).
+__device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
+                                            float l_run, bool beaten) {
+    const AttnArgs& a = *c.a;
+    const int lane = c.lane;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);   // a head spans lanes l and l ^ 32
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int h = 32 * c.wave + (lane & 31);
+    const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h;
+    __bf16* dst = reinterpret_cast<__bf16*>(a.o) + orow * kLatent + 4 * (lane >> 5);
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<bf16x4*>(dst + 32 * cb + 8 * gq) =
+                to_bf16x4(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv, acc[cb][4 * gq + 2] * inv,
+                          acc[cb][4 * gq + 3] * inv);
+    // A head whose reference was beaten by more than 32 is marked with a
+    // negative sum; the merge recomputes it exactly.
+    beaten = beaten || __shfl_xor((int)beaten, 32);
+    if (lane < 32) {
+        a.m_part[orow] = m_ref;
+        a.l_part[orow] = beaten ? -1.f : l_tot;
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
+    __shared__ __attribute__((aligned(1024))) unsigned char tiles[kBufs * kBufBytes];
+    __shared__ int sidx[kMaxSlotsPerSplit];
+
+    // Workgroup -> (query row, split).  Consecutive workgroups land on the 8
+    // XCDs in turn; the splits of one query row share an XCD, so its absorbed
+    // query is read from HBM once.  Latest query rows (most work) go first.
+    const int id = blockIdx.x;
+    const int split = (id >> 3) % a.n_split;
+    const int rr = ((id >> 3) / a.n_split) * 8 + (id & 7);
+    if (rr >= a.R) return;
+
+    SplitCtx c;
+    c.a = &a;
+    c.tiles = tiles;
+    c.sidx = sidx;
+    c.r = (a.R - 1) - rr;
+    c.split = split;
+    c.wave = wave_id();
+    c.lane = threadIdx.x & 63;
+    const int slot_begin = split * a.slots_per_split;
+    const int nslots = min(a.k, slot_begin + a.slots_per_split) - slot_begin;   // >= 1
+    c.ntiles = (nslots + kRows - 1) / kRows;
+    c.limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + c.r;
+    c.T = a.T;
+    c.kv_desc = make_desc(reinterpret_cast<const __bf16*>(a.kv) + (size_t)c.r * a.cache_rows_per_query * kLatent,
+                          (unsigned)c.T * (kLatent * 2));
+    c.pe_desc = make_desc(reinterpret_cast<const __bf16*>(a.pe) + (size_t)c.r * a.cache_rows_per_query * kRope,
+                          (unsigned)c.T * (kRope * 2));
+    c.qrow = reinterpret_cast<const __bf16*>(a.q) +
+             ((size_t)c.r * kHeads + 32 * c.wave + (c.lane & 31)) * kQRow + 8 * (c.lane >> 5);
+
+    // Index list of this split into LDS (-1 past its end).
+    {
+        const int32_t* src = a.idx + (size_t)c.r * a.k + slot_begin;
+        for (int i = threadIdx.x; i < c.ntiles * kRows; i += 256) sidx[i] = i < nslots ? src[i] : -1;
+    }
+    __syncthreads();
+
+    f32x16 acc[16];
+    float m_ref = -INFINITY, l_run = 0.f;
+    bool beaten = false;
+    attn_pass(c, m_ref, acc, l_run, beaten);
+    attn_finish(c, acc, m_ref, l_run, beaten);
+}
+
+// --------------------------------------------------------------------------
+// Step 4 merge + step 5: out[r, h, :] = O~[r, h, :] . W_UV[h]^T
+//
+// Per head a [R x 512] . [512 x 128] product, computed transposed:
+// out^T = W_UV[h] . O~^T, so W_UV rows (d) are the A operand, loaded straight
+// from HBM with 16-byte reads (c is contiguous in the weight).  Workgroup =
+// (head, group of 32-row query blocks); wave w owns 32 values d and keeps its
+// W_UV slice (32 x 512) in registers.  Each 32-row block of O~ is staged in
+// LDS as bf16 once per workgroup: copied when the index list was not split,
+// else merged from the split partials.
+// --------------------------------------------------------------------------
+constexpr int kORow = 1040;   // bytes per staged O~ row (512 bf16 + pad)
+
+// Merge the split partials of one (query row, head), 8 columns starting at 8*ch.
+// Split s holds its normalised mix O~_s (bf16), its running max m_s (log2
+// domain) and its probability sum l_s; the merged row is
+// sum_s w_s O~_s / sum_s w_s with w_s = l_s * 2^(m_s - max_s m_s).
+__device__ __forceinline__ bf16x8 merge_partials(const __bf16* o_part, const float* m_part,
+                                                 const float* l_part, int R, int n_split, int rr,
+                                                 int h, int ch) {
+    float mmax = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp) mmax = fmaxf(mmax, m_part[((size_t)sp * R + rr) * kHeads + h]);
+    float W = 0.f;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (mmax != -INFINITY) {
+        for (int sp = 0; sp < n_split; ++sp) {
+            const size_t o = ((size_t)sp * R + rr) * kHeads + h;
+            const float ls = l_part[o];
+            if (!(ls > 0.f)) continue;
+            const float wgt = ls * exp2f(m_part[o] - mmax);
+            W += wgt;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(o_part + o * kLatent + 8 * ch);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[q] += wgt * (float)v[q];
+        }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    bf16x8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (__bf16)(x[q] * inv);
+    return v;
+}
+
+// Exact mix of one (query row, head) in float32, for a head whose first-tile
+// reference was beaten by more than 2^32 during the attention pass: pass one
+// finds the maximum score over the row's whole index list, pass two weighs and
+// mixes the selected latent rows (one 256-slot chunk at a time).  The result,
+// normalised, is written to out[0..511].  All 256 threads take part.
+__device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* red, float* p_s,
+                          int* pos_s) {
+    const int tid = threadIdx.x;
+    const __bf16* q = reinterpret_cast<const __bf16*>(a.q) + ((size_t)rr * kHeads + h) * kQRow;
+    const __bf16* kv = reinterpret_cast<const __bf16*>(a.kv) + (size_t)rr * a.cache_rows_per_query * kLatent;
+    const __bf16* pe = reinterpret_cast<const __bf16*>(a.pe) + (size_t)rr * a.cache_rows_per_query * kRope;
+    const int32_t* idx = a.idx + (size_t)rr * a.k;
+    const int limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + rr;
+    auto score = [&](int t) {
+        float d = 0.f;
+        for (int c = 0; c < kLatent; ++c) d += (float)q[c] * (float)kv[(size_t)t * kLatent + c];
+        for (int c = 0; c < kRope; ++c) d += (float)q[kLatent + c] * (float)pe[(size_t)t * kRope + c];
+        return d * a.scale_log2;
+    };
+    auto block_max = [&](float v) {
+        for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+        __syncthreads();
+        if ((tid & 63) == 0) red[tid >> 6] = v;
+        __syncthreads();
+        return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    };
+    float m = -INFINITY;
+    for (int base = 0; base < a.k; base += 256) {
+        const int slot = base + tid;
+        const int t = slot < a.k ? idx[slot] : -1;
+        if (t >= 0 && t < a.T && t <= limit) m = fmaxf(m, score(t));
+    }
+    m = block_max(m);
+    float acc0 = 0.f, acc1 = 0.f, lp = 0.f;
+    for (int base = 0; base < a.k; base += 256) {
+        const int slot = base + tid;
+        int t = slot < a.k ? idx[slot] : -1;
+        if (!(t >= 0 && t < a.T && t <= limit)) t = -1;
+        const float p = t >= 0 ? exp2f(score(t) - m) : 0.f;
+        lp += p;
+        __syncthreads();
+        p_s[tid] = p;
+        pos_s[tid] = t;
+        __syncthreads();
+        for (int jj = 0; jj < 256; ++jj) {
+            const int tj = pos_s[jj];
+            if (tj < 0) continue;
+            acc0 += p_s[jj] * (float)kv[(size_t)tj * kLatent + tid];
+            acc1 += p_s[jj] * (float)kv[(size_t)tj * kLatent + tid + 256];
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) lp += __shfl_xor(lp, o);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = lp;
+    __syncthreads();
+    const float L = red[0] + red[1] + red[2] + red[3];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    out[tid] = acc0 * inv;
+    out[tid + 256] = acc1 * inv;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
+                                               __bf16* __restrict__ out, int r_groups) {
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[32 * kORow];
+    __shared__ float xo[kLatent];
+    __shared__ float xred[4];
+    __shared__ float xp[256];
+    __shared__ int xpos[256];
+    __shared__ int marked[32];
+    const void* o_ws = a.o;
+    const float* m_part = a.m_part;
+    const float* l_part = a.l_part;
+    const int R = a.R;
+    const int n_split = a.n_split;
+    const int h = blockIdx.x;
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int d = 32 * wave + (lane & 31);
+
+    bf16x8 wa[32];
+    {
+        const __bf16* wrow = w_uv + ((size_t)h * kValue + d) * kLatent + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
+    }
+
+    for (int rb = blockIdx.y; rb * 32 < R; rb += r_groups) {
+        // stage O~ rows rb*32 .. +31 of head h: 32 rows x 64 chunks of 8 columns
+        if (n_split == 1) {
+            u32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = threadIdx.x + 256 * i;
+                const int rr = rb * 32 + (e >> 6);
+                v[i] = rr < R ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(o_ws) +
+                                                                 ((size_t)rr * kHeads + h) * kLatent + 8 * (e & 63))
+                              : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = threadIdx.x + 256 * i;
+                *reinterpret_cast<u32x4*>(obuf + (e >> 6) * kORow + 16 * (e & 63)) = v[i];
+            }
+        } else {
+            for (int e = threadIdx.x; e < 32 * 64; e += 256) {
+                const int rr = rb * 32 + (e >> 6);
+                const bf16x8 v = rr < R ? merge_partials(reinterpret_cast<const __bf16*>(o_ws), m_part,
+                                                         l_part, R, n_split, rr, h, e & 63)
+                                        : bf16x8{};
+                *reinterpret_cast<bf16x8*>(obuf + (e >> 6) * kORow + 16 * (e & 63)) = v;
+            }
+        }
+        // heads whose attention pass was marked inexact: recompute exactly
+        if (threadIdx.x < 32) {
+            const int rr = rb * 32 + threadIdx.x;
+            int bad = 0;
+            if (rr < R)
+                for (int sp = 0; sp < n_split; ++sp) bad |= l_part[((size_t)sp * R + rr) * kHeads + h] < 0.f;
+            marked[threadIdx.x] = bad;
+        }
+        __syncthreads();
+        for (int row = 0; row < 32; ++row) {
+            if (!marked[row]) continue;
+            exact_mix(a, rb * 32 + row, h, xo, xred, xp, xpos);
+            for (int c = threadIdx.x; c < kLatent; c += 256)
+                *reinterpret_cast<__bf16*>(obuf + row * kORow + 2 * c) = (__bf16)xo[c];
+            __syncthreads();
+        }
+        f32x16 acc = {};
+        const unsigned char* brow = obuf + (lane & 31) * kORow + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + 32 * ks);
+            acc = mfma32(wa[ks], bv, acc);
+        }
+        const int r = rb * 32 + (lane & 31);
+        if (r < R) {
+            __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
+                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                              int R, hipStream_t s) {
+    const int blocks = (R + 31) / 32;
+    const int r_groups = blocks < 4 ? blocks : 4;
+    hipLaunchKernelGGL(absorb_q_bf16, dim3(kHeads * 4, r_groups), dim3(256), 0, s,
+                       static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_pe),
+                       static_cast<const __bf16*>(w_uk), static_cast<__bf16*>(q_out), R, r_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+    const int row_groups = (a.R + 7) / 8;
+    hipLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, a, row_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s) {
+    const int blocks = (a.R + 31) / 32;
+    const int r_groups = blocks < 8 ? blocks : 8;
+    hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, a,
+                       static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(out), r_groups);
+    return hipGetLastError();
+}
+
+}  // namespace mla

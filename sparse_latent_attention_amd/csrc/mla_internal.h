@@ -1,0 +1,68 @@
+// Internal declarations shared by the host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kHeads = 128;   // n_heads
+constexpr int kLatent = 512;  // kv_lora_rank: width of the cached latent c^KV
+constexpr int kRope = 64;     // qk_rope_head_dim: width of the shared rotary key
+constexpr int kNope = 128;    // qk_nope_head_dim
+constexpr int kValue = 128;   // v_head_dim
+constexpr int kQRow = kLatent + kRope;  // 576: absorbed query row [q_c | q_pe]
+
+// Attention work split: a workgroup owns all heads of one query row and one
+// split of that row's index list; splits hold whole tiles of kTileRows slots
+// and at most kMaxSlotsPerSplit slots.
+constexpr int kTileRows = 32;
+constexpr int kMaxSlotsPerSplit = 2048;
+// Largest cache length: gathers address one query's cache with 32-bit byte
+// offsets that must stay below 2^31.
+constexpr int kMaxT = (1 << 21) - 1;
+
+// Workspace carve-up, shared by the size query and the launchers.
+struct Workspace {
+    size_t q_off, q_bytes;        // absorbed queries [R, 128, 576] in the call dtype
+    size_t o_off, o_bytes;        // mixed latent per split [n_split, R, 128, 512]
+    size_t ml_off, ml_bytes;      // per split reference max / probability sum [n_split, R, 128] x2 (f32)
+    size_t total;
+    int n_split;                  // splits of each row's index list
+    int slots_per_split;          // index-list slots per split (multiple of kTileRows)
+};
+
+Workspace plan_workspace(int rows, int k, int dtype);
+
+struct AttnArgs {
+    const void* q;          // [R, 128, 576] absorbed queries
+    const void* kv;         // latent cache base
+    const void* pe;         // rotary cache base
+    const int32_t* idx;     // [R, k]
+    long long cache_rows_per_query;  // cache row stride between queries (0 = shared cache)
+    int R, T, k;
+    int causal_base;        // -1: no causal bound; else query r sees positions <= causal_base + r
+    float scale_log2;       // softmax_scale * log2(e)
+    int n_split, slots_per_split;
+    void* o;                // see Workspace::o
+    float* m_part;          // [n_split, R, 128]
+    float* l_part;          // [n_split, R, 128]
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                              int R, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s);
+
+hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                             int R, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,
+                         const void* w_uv, void* out, int R, int n_split, hipStream_t s);
+
+hipError_t launch_validate(const int32_t* idx, int rows, int k, int T, int allow_pad, int* flag,
+                           hipStream_t s);
+
+}  // namespace mla

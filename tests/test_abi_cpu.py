@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI: no GPU, no kernel launches.
+
+Every call below either is a pure size query or fails a host-side argument
+check before anything is launched, so it runs without a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_latent_attention_amd import _lib
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                   "mla_sparse.h")
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HDR).read()
+    return re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = set(declared_functions())
+    assert {"mla_sparse_decode", "mla_sparse_prefill_chunk", "mla_sparse_decode_workspace_size",
+            "mla_sparse_prefill_chunk_workspace_size", "mla_validate_indices",
+            "mla_status_string", "mla_set_attention_events", "mla_abi_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.mla_status_string(code).decode().startswith(name)
+    assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
+    assert lib.mla_abi_version() == 1
+
+
+def ws_expected(rows, esize, n_split):
+    """Absorbed queries, per-split mixes (bf16 or f32), per-split max and sum."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    q = rows * 128 * 576 * esize
+    o = n_split * rows * 128 * 512 * esize
+    ml = 2 * n_split * rows * 128 * 4
+    return up(up(up(q) + o) + ml)
+
+
+def test_workspace_size_plan(lib):
+    # 64 rows: 4 splits of 512 slots fill the 256 compute units
+    assert lib.mla_sparse_decode_workspace_size(64, 32768, 2048, 1) == ws_expected(64, 2, 4)
+    # 32 rows: 8 splits of 256 slots
+    assert lib.mla_sparse_decode_workspace_size(32, 8192, 2048, 1) == ws_expected(32, 2, 8)
+    # one row, 1001 slots: splits capped by the 32-slot tile count
+    assert lib.mla_sparse_decode_workspace_size(1, 1001, 1001, 1) == ws_expected(1, 2, 32)
+    assert lib.mla_sparse_decode_workspace_size(1, 64, 64, 0) == ws_expected(1, 4, 2)
+    # 4096 queries: one split each; splits never exceed 2048 slots
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 4096, 2048, 1) == ws_expected(4096, 2, 1)
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 8192, 4096, 1) == ws_expected(4096, 2, 2)
+    # invalid arguments report zero
+    assert lib.mla_sparse_decode_workspace_size(0, 10, 5, 1) == 0
+    assert lib.mla_sparse_decode_workspace_size(1, 10, 11, 1) == 0
+    assert lib.mla_sparse_decode_workspace_size(1, 10, 5, 7) == 0
+    assert lib.mla_sparse_prefill_chunk_workspace_size(1, 10, 0, 1) == 0
+
+
+def call_decode(lib, **kw):
+    args = dict(q_nope=FAKE, q_pe=FAKE, kv=FAKE, pe=FAKE, idx=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE,
+                B=2, T=100, ld_T=100, k=10, scale=0.07, dtype=1, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.mla_sparse_decode(args["q_nope"], args["q_pe"], args["kv"], args["pe"], args["idx"],
+                                 args["w_uk"], args["w_uv"], args["out"], args["B"], args["T"],
+                                 args["ld_T"], args["k"], args["scale"], args["dtype"], args["ws"],
+                                 args["ws_bytes"], args["stream"])
+
+
+def call_prefill(lib, **kw):
+    args = dict(q_nope=FAKE, q_pe=FAKE, kv=FAKE, pe=FAKE, idx=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE,
+                S=4, T=100, k=10, start=0, scale=0.07, dtype=1, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.mla_sparse_prefill_chunk(args["q_nope"], args["q_pe"], args["kv"], args["pe"],
+                                        args["idx"], args["w_uk"], args["w_uv"], args["out"],
+                                        args["S"], args["T"], args["k"], args["start"],
+                                        args["scale"], args["dtype"], args["ws"],
+                                        args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("field", ["q_nope", "q_pe", "kv", "pe", "idx", "w_uk", "w_uv", "out"])
+def test_null_pointers_rejected(lib, field):
+    assert call_decode(lib, **{field: None}) == 1
+    assert call_prefill(lib, **{field: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(k=0), dict(k=101), dict(ld_T=99),
+                                dict(scale=float("nan")), dict(scale=float("inf"))])
+def test_decode_shape_errors(lib, kw):
+    assert call_decode(lib, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(S=0), dict(T=0), dict(k=0), dict(start=-1),
+                                dict(start=97, S=4), dict(scale=float("nan"))])
+def test_prefill_shape_errors(lib, kw):
+    assert call_prefill(lib, **kw) == 2
+
+
+def test_dtype_and_alignment_errors(lib):
+    assert call_decode(lib, dtype=2) == 4
+    assert call_prefill(lib, dtype=-1) == 4
+    for field in ["q_nope", "kv", "idx", "w_uv", "out"]:
+        assert call_decode(lib, **{field: MISALIGNED}) == 3
+        assert call_prefill(lib, **{field: MISALIGNED}) == 3
+
+
+def test_workspace_errors(lib):
+    need = lib.mla_sparse_decode_workspace_size(2, 100, 10, 1)
+    assert call_decode(lib, ws_bytes=need - 1) == 5
+    assert call_decode(lib, ws=None, ws_bytes=need) == 5
+    assert call_decode(lib, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == 5   # not 256-aligned
+    need_p = lib.mla_sparse_prefill_chunk_workspace_size(4, 100, 10, 1)
+    assert call_prefill(lib, ws_bytes=need_p - 1) == 5
+
+
+def test_validator_and_event_hook_argument_checks(lib):
+    assert lib.mla_validate_indices(None, 1, 1, 1, 0, FAKE, None) == 1
+    assert lib.mla_validate_indices(FAKE, 0, 1, 1, 0, FAKE, None) == 2
+    assert lib.mla_validate_indices(MISALIGNED, 1, 1, 1, 0, FAKE, None) == 3
+    assert lib.mla_set_attention_events(FAKE, None) == 1
+    assert lib.mla_set_attention_events(None, None) == 0
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "absent.so"))

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle.
+
+Tolerance (per tensor): max|gpu - oracle| / max|oracle| <= 1e-5 for float32
+inputs and <= 2e-2 for bf16 inputs.  Small configurations are compared on
+every output; full-size configurations on sampled query rows, in the same
+launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from synth.generators import DecodeConfig, PrefillConfig  # noqa: E402
+
+from .gpu_util import TOL, log, rel_err, to_dev, to_host64  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_latent_attention_amd as m
+    m._lib.load()
+    return m
+
+
+def upload(inp):
+    return {k: to_dev(v) for k, v in inp.items()}
+
+
+def run_decode(mla, dev, **kw):
+    out = mla.decode(dev["q_nope"], dev["q_pe"], dev["kv_cache"], dev["pe_cache"], dev["topk_idx"],
+                     dev["w_uk"], dev["w_uv"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_prefill(mla, dev, start_pos, **kw):
+    out = mla.prefill_chunk(dev["q_nope"], dev["q_pe"], dev["kv_cache"], dev["pe_cache"],
+                            dev["topk_idx"], dev["w_uk"], dev["w_uv"], start_pos=start_pos, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_decode(mla, cfg, rows=None, inp=None, dev=None):
+    inp = synth.decode_inputs(cfg) if inp is None else inp
+    dev = upload(inp) if dev is None else dev
+    assert np.array_equal(dev["topk_idx"].cpu().numpy(), inp["topk_idx"])   # indices bit-exact
+    log(f"decode {cfg.name}: B={cfg.B} T={cfg.T} k={cfg.k} {cfg.dtype}")
+    out = to_host64(run_decode(mla, dev))
+    rows = list(range(cfg.B)) if rows is None else rows
+    ref = oracle.decode(inp, rows=rows)
+    err = rel_err(out[rows], ref)
+    log(f"  rows {rows[:8]}{'...' if len(rows) > 8 else ''}: rel err {err:.3e} (tol {TOL[cfg.dtype]})")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[cfg.dtype]
+    return out, inp, dev
+
+
+# ------------------------------------------------------------------ configs
+def test_config0_tiny_dense_f32(mla):
+    check_decode(mla, synth.CONFIGS["tiny_dense_f32"])
+
+
+def test_config1_page_shape_dense(mla):
+    check_decode(mla, synth.CONFIGS["page_dense_bf16"])
+
+
+def test_config2_sparse_b32(mla):
+    check_decode(mla, synth.CONFIGS["sparse_b32_t8k"], rows=[0, 1, 7, 16, 30, 31])
+
+
+def test_config3_headline_sampled(mla):
+    check_decode(mla, synth.CONFIGS["sparse_b64_t32k"], rows=[0, 21, 42, 63])
+
+
+def test_config4_prefill_sampled(mla):
+    cfg = synth.CONFIGS["prefill_s4096"]
+    inp = synth.prefill_inputs(cfg)
+    dev = upload(inp)
+    assert np.array_equal(dev["topk_idx"].cpu().numpy(), inp["topk_idx"])
+    log(f"prefill {cfg.name}: S={cfg.S} T={cfg.T} k={cfg.k}")
+    out = to_host64(run_prefill(mla, dev, cfg.start_pos))
+    rows = [0, 1, 2, 63, 64, 1000, 2046, 2047, 2048, 3333, 4095]
+    ref = oracle.prefill(inp, rows=rows, start_pos=cfg.start_pos)
+    err = rel_err(out[rows], ref)
+    log(f"  rows {rows}: rel err {err:.3e}")
+    assert np.all(np.isfinite(out)) and err <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ ragged and small
+def test_ragged_bf16_all_rows(mla):
+    check_decode(mla, DecodeConfig(10, "ragged", B=3, T=777, k=333, dtype="bf16"))
+
+
+def test_sparse_f32_all_rows(mla):
+    check_decode(mla, DecodeConfig(11, "f32sparse", B=2, T=300, k=100, dtype="f32"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_small_all_rows(mla, dtype):
+    cfg = PrefillConfig(12, "prefill_small", S=70, T=300, k=48, start_pos=200, dtype=dtype)
+    inp = synth.prefill_inputs(cfg)
+    dev = upload(inp)
+    out = to_host64(run_prefill(mla, dev, cfg.start_pos))
+    ref = oracle.prefill(inp, start_pos=cfg.start_pos)
+    err = rel_err(out, ref)
+    log(f"prefill small {dtype}: rel err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_prefill_from_position_zero_all_rows(mla):
+    cfg = PrefillConfig(13, "prefill_zero", S=150, T=150, k=100, start_pos=0, dtype="bf16")
+    inp = synth.prefill_inputs(cfg)
+    out = to_host64(run_prefill(mla, upload(inp), 0))
+    err = rel_err(out, oracle.prefill(inp, start_pos=0))
+    log(f"prefill from 0: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_selected_row(mla, dtype):
+    check_decode(mla, DecodeConfig(14, "k1", B=2, T=50, k=1, dtype=dtype))
+
+
+def test_empty_slots_and_empty_selection(mla):
+    cfg = DecodeConfig(15, "pads", B=3, T=200, k=40, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    inp["topk_idx"][0, ::3] = -1          # some empty slots
+    inp["topk_idx"][1, :] = -1            # nothing selected: all-zero output
+    out, _, _ = check_decode(mla, cfg, rows=[0, 2], inp=inp)
+    assert np.array_equal(out[1], np.zeros((128, 128)))
+
+
+def test_unselected_rows_never_read(mla):
+    cfg = DecodeConfig(16, "poison", B=2, T=500, k=90, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    clean = to_host64(run_decode(mla, upload(inp)))
+    poisoned = {k: v.copy() for k, v in inp.items()}
+    for b in range(cfg.B):
+        mask = np.ones(cfg.T, bool)
+        mask[inp["topk_idx"][b]] = False
+        poisoned["kv_cache"][b, mask] = 0x7FC0     # bf16 NaN
+        poisoned["pe_cache"][b, mask] = 0x7F80     # bf16 +inf
+    got = to_host64(run_decode(mla, upload(poisoned)))
+    assert np.array_equal(got, clean)
+
+
+def test_rows_beyond_T_never_read(mla):
+    cfg = DecodeConfig(17, "ldT", B=2, T=300, k=60, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    dev = upload(inp)
+    ld = cfg.T + 17
+    big_kv = torch.full((cfg.B, ld, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    big_pe = torch.full((cfg.B, ld, 64), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    big_kv[:, :cfg.T] = dev["kv_cache"]
+    big_pe[:, :cfg.T] = dev["pe_cache"]
+    ref = to_host64(run_decode(mla, dev))
+    dev2 = dict(dev, kv_cache=big_kv, pe_cache=big_pe)
+    idx = dev["topk_idx"].clone()
+    idx[:, 0] = cfg.T + 5                 # at or past T: treated as an empty slot
+    dev2["topk_idx"] = idx
+    got = to_host64(mla.decode(dev2["q_nope"], dev2["q_pe"], big_kv, big_pe, idx, dev2["w_uk"],
+                               dev2["w_uv"], T=cfg.T))
+    assert np.all(np.isfinite(got))
+    idx_ref = idx.cpu().numpy()
+    idx_ref[idx_ref >= cfg.T] = -1        # the library's reading: an empty slot
+    inp2 = dict(inp, topk_idx=idx_ref)
+    err = rel_err(got, oracle.decode(inp2))
+    assert err <= TOL["bf16"]
+    assert not np.array_equal(got, ref)
+
+
+def test_index_order_does_not_matter(mla):
+    cfg = DecodeConfig(18, "perm", B=2, T=2000, k=300, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    rng = np.random.default_rng(1)
+    shuffled = dict(inp, topk_idx=np.stack([rng.permutation(r) for r in inp["topk_idx"]]))
+    out = to_host64(run_decode(mla, upload(shuffled)))
+    assert rel_err(out, oracle.decode(inp)) <= TOL["bf16"]
+
+
+def test_repeat_calls_are_bit_identical_and_workspace_contents_ignored(mla):
+    cfg = DecodeConfig(19, "det", B=5, T=3000, k=700, dtype="bf16")
+    dev = upload(synth.decode_inputs(cfg))
+    a = run_decode(mla, dev).clone()
+    need = mla.decode_workspace_size(cfg.B, cfg.T, cfg.k, torch.bfloat16)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda:0")
+    b = run_decode(mla, dev, workspace=ws)
+    c = run_decode(mla, dev, workspace=ws)
+    assert torch.equal(a, b) and torch.equal(b, c)
+
+
+def test_validate_indices(mla):
+    idx = torch.tensor([[0, 5, 9, 3], [1, 2, 3, 4]], dtype=torch.int32, device="cuda:0")
+    assert mla.validate_indices(idx, T=10) == 0
+    dup = idx.clone()
+    dup[1, 3] = 1
+    assert mla.validate_indices(dup, T=10) == 2
+    assert mla.validate_indices(idx, T=9) == 1
+    pad = idx.clone()
+    pad[0, 1] = -1
+    assert mla.validate_indices(pad, T=10) == 1
+    assert mla.validate_indices(pad, T=10, allow_pad=True) == 0
+    inp = synth.decode_inputs(synth.CONFIGS["sparse_b32_t8k"], with_cache=False)
+    assert mla.validate_indices(to_dev(inp["topk_idx"]), T=8192) == 0
+
+
+def test_attention_event_hook(mla):
+    cfg = DecodeConfig(20, "ev", B=4, T=1000, k=256, dtype="bf16")
+    dev = upload(synth.decode_inputs(cfg))
+    b = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    b.record()
+    e.record()
+    torch.cuda.synchronize()
+    mla.set_attention_events(b, e)
+    run_decode(mla, dev)
+    ms = b.elapsed_time(e)
+    assert 0.0 < ms < 1000.0
+
+
+def test_large_logits_take_the_exact_path(mla):
+    # With W_UK = 0 the scores are scale * (q_pe . k_R), computed from exact bf16
+    # inputs, so a large scale spreads them over tens of log2 units without
+    # amplifying any rounding.  Later tiles then beat the first tile's reference
+    # by more than 2^32 for many heads, and the merge recomputes those exactly.
+    cfg = DecodeConfig(21, "big_logits", B=64, T=2000, k=1024, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    inp["w_uk"] = np.zeros_like(inp["w_uk"])
+    scale = 3.0
+    out = to_host64(run_decode(mla, upload(inp), softmax_scale=scale))
+    rows = [0, 17, 40, 63]
+    ref = oracle.decode(inp, rows=rows, scale=scale)
+    err = rel_err(out[rows], ref)
+    log(f"large logits: rel err {err:.3e}")
+    assert np.all(np.isfinite(out)) and err <= TOL["bf16"]
+
+
+def test_moderate_scale(mla):
+    cfg = DecodeConfig(22, "scale_half", B=8, T=2000, k=1024, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    out = to_host64(run_decode(mla, upload(inp), softmax_scale=0.5))
+    ref = oracle.decode(inp, rows=[0, 7], scale=0.5)
+    assert rel_err(out[[0, 7]], ref) <= TOL["bf16"]
