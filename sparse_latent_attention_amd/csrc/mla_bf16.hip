@@ -332,32 +332,40 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         __builtin_amdgcn_s_barrier();   // every wave's gathers of t landed; t-1 fully read
         if (t + 3 < ntiles) gather_tile(c, t + 3);
 
-        const lds_u8* buf = (const lds_u8*)c.tiles + (t & (kBufs - 1)) * kBufBytes;
+        // Per-tile bases (buffer offset folded in before the XOR, which keeps
+        // the swizzled addresses from being hoisted as loop invariants).
+        const int bo = (t & (kBufs - 1)) * kBufBytes;
+        const lds_u8* buf = (const lds_u8*)c.tiles;
+        const int sc_t = sc_base + bo, pe_t = pe_base + bo;
+        const int tr_t[2][2] = {{tr_base[0][0] + bo, tr_base[0][1] + bo}, {tr_base[1][0] + bo, tr_base[1][1] + bo}};
         const int pv = c.sidx[t * kRows + j];
         const unsigned vmask =
             (unsigned)__builtin_amdgcn_ballot_w64(pv >= 0 && pv < c.T && pv <= c.limit);
 
-        // ---- scores S^T (rows x heads), accumulated in ordinary VGPRs
+        // ---- scores S^T (rows x heads), accumulated in ordinary VGPRs.  The
+        // asm MFMAs keep their order, so operands are read four MFMAs ahead.
+        auto sc_read = [&](int ks) -> bf16x8 {
+            if (ks < 32)
+                return *(const __attribute__((address_space(3))) bf16x8*)(
+                    buf + ((sc_t ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+            return *(const __attribute__((address_space(3))) bf16x8*)(buf + (pe_t ^ ((ks - 32) << 5)));
+        };
+        bf16x8 pre[4] = {sc_read(0), sc_read(1), sc_read(2), sc_read(3)};
         f32x16 sacc;
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-            const bf16x8 av = *(const __attribute__((address_space(3))) bf16x8*)(
-                buf + ((sc_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+        for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8 av = pre[ks & 3];
+            if (ks + 4 < 36) pre[ks & 3] = sc_read(ks + 4);
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
             else mfma32_v(sacc, av, qf[ks]);
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 av =
-                *(const __attribute__((address_space(3))) bf16x8*)(buf + (pe_base ^ (ks << 5)));
-            mfma32_v(sacc, av, qf[32 + ks]);
-        }
         mfma_settle(sacc);
+        // validity of this lane's rows 8*(i/4) + 4*hsel + i%4
+        const unsigned vml = vmask >> (4 * hsel);
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = 8 * (i >> 2) + 4 * hsel + (i & 3);
-            const bool ok = (vmask >> row) & 1u;
+            const bool ok = (vml >> (8 * (i >> 2) + (i & 3))) & 1u;
             sacc[i] = ok ? sacc[i] * c.a->scale_log2 : -INFINITY;
             mx = fmaxf(mx, sacc[i]);
         }
@@ -376,16 +384,19 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         }
         l_run += psum;
 
-        // ---- mix: O~^T[c][h] += V^T[c][j] P^T[j][h]
+        // ---- mix: O~^T[c][h] += V^T[c][j] P^T[j][h]; V^T fragments read three
+        // MFMAs ahead
+        auto tr_read = [&](int m) -> bf16x8 {
+            const int cb = m >> 1, kc = m & 1;
+            const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
+            return cat(lds_read_tr(buf + ((tr_t[kc][0] ^ x) + y)), lds_read_tr(buf + ((tr_t[kc][1] ^ x) + y)));
+        };
+        bf16x8 vpre[3] = {tr_read(0), tr_read(1), tr_read(2)};
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb) {
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
-                const bf16x8 av = cat(lds_read_tr(buf + ((tr_base[kc][0] ^ x) + y)),
-                                      lds_read_tr(buf + ((tr_base[kc][1] ^ x) + y)));
-                acc[cb] = mfma32(av, pb[kc], acc[cb]);
-            }
+        for (int m = 0; m < 32; ++m) {
+            const bf16x8 av = vpre[m % 3];
+            if (m + 3 < 32) vpre[m % 3] = tr_read(m + 3);
+            acc[m >> 1] = mfma32(av, pb[m & 1], acc[m >> 1]);
         }
     }
     MLA_WAIT_VMCNT(0);
