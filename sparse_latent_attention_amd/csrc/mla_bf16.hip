@@ -51,16 +51,21 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
 // accumulator takes all 256 accumulation registers, so the compiler (which
 // picks one MFMA register form per kernel) would otherwise shuttle the score
 // tile through them.  Chained MFMAs that read the previous result as their
-// accumulator input (exact overlap) need no wait states; mfma_settle covers
-// the MFMA-write -> VALU-read window before the scores are read.
+// accumulator input (exact overlap) need no wait states.  The compiler does
+// not see these as MFMAs, so the last one of a chain carries the wait states
+// an MFMA result needs before any other instruction may read it; the result
+// is not available to the compiler before that.
 __device__ __forceinline__ void mfma32_v_first(f32x16& d, bf16x8 a, bf16x8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_v(f32x16& d, bf16x8 a, bf16x8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_settle(f32x16& d) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+// The final MFMA writes a separate register tuple, so that no copy of the
+// chain's accumulator can be placed before the chain has finished.
+__device__ __forceinline__ void mfma32_v_last(f32x16& out, const f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "=&v"(out) : "v"(a), "v"(b), "v"(d));
 }
 
 // Transposing read of four bf16 (see the header comment).
@@ -253,33 +258,19 @@ struct SplitCtx {
     int r, split, ntiles, limit, T, wave, lane;
 };
 
-// Gather tile t into buffer t % kBufs: wave w fetches rows 8w .. 8w+7 (eight
-// 1 KiB latent rows, then one instruction for their rotary parts).  Empty or
-// out-of-range slots use an out-of-range offset: no memory is touched.
-__device__ __forceinline__ void gather_tile(const SplitCtx& c, int t) {
-    unsigned char* buf = c.tiles + (t & (kBufs - 1)) * kBufBytes;
-    // Opaque copy of the lane id: keeps the per-row lane offsets from being
-    // hoisted out of the tile loop (they would pin eight registers).
-    int ln = c.lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = 8 * c.wave + q;
-        const int p = c.sidx[t * kRows + row];
-        const bool ok = p >= 0 && p < c.T && p <= c.limit;
-        const unsigned off = ok ? (unsigned)p * 1024u + ((unsigned)(ln ^ lat_swz(row)) << 4) : kOutOfRange;
-        load_lds16(c.kv_desc, (unsigned)(size_t)(buf + row * 1024), off);
-    }
-    const int jp = ln >> 3;
-    const int p = c.sidx[t * kRows + 8 * c.wave + jp];
-    const bool ok = p >= 0 && p < c.T && p <= c.limit;
-    const unsigned off = ok ? (unsigned)p * 128u + ((unsigned)((ln & 7) ^ jp) << 4) : kOutOfRange;
-    load_lds16(c.pe_desc, (unsigned)(size_t)(buf + kLatBytes + c.wave * kPeBlock), off);
-}
+// A head whose per-tile probability sum exceeds this (relative to its
+// reference) is recomputed exactly by the merge; below it, no probability or
+// partial sum comes near the float/bf16 range.
+constexpr float kBeatenSum = 4294967296.f;   // 2^32
 
-// One pass over the split's tiles: accumulate against a reference taken from
-// each head's first tile with a selected row; `beaten` reports a tile that
-// beat it by more than 32 (log2 units).
+// One pass over the split's tiles.  Software pipeline, per iteration t:
+//   wait for tile t+1, barrier, then the score MFMAs of tile t+1 run with the
+//   softmax of tile t and the gather of tile t+3 interleaved between them
+//   (VALU and memory instructions issue while an MFMA executes), then the mix
+//   MFMAs of tile t.
+// The reference of each head is the (scaled) maximum of its first tile with
+// a selected row; no rescaling happens afterwards.  `beaten` reports a tile
+// whose probabilities exceeded kBeatenSum against that reference.
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
                                           float& l_run, bool& beaten) {
     const int lane = c.lane;
@@ -316,80 +307,115 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             tr_base[kc][t] = row * 1024 + (e4 << 6) + ((lo ^ (2 * t + g)) << 4) + (q4 & 1) * 8;
         }
 
+    // A slot is selected iff 0 <= p < lim (p < T and, for prefill, p <= limit).
+    const unsigned lim = min((unsigned)c.T, (unsigned)c.limit + 1u);
+    const lds_u8* tiles = (const lds_u8*)c.tiles;
+    const unsigned tiles_addr = (unsigned)(size_t)c.tiles;
+    const int jp = lane >> 3;                          // rotary row of this lane's gather
+    const unsigned pe_lane = (unsigned)(((lane & 7) ^ jp) << 4);
+
+    // Gathers.  Lane l reads the index of row 8*wave + l/8 of the tile: it
+    // addresses that row's rotary part, and lanes 8q .. 8q+7 hold the index of
+    // latent row q, which is read back as a wave-uniform value.  A tile index
+    // >= ntiles issues the same nine loads with out-of-range offsets (they
+    // touch no memory), so every gather adds exactly nine to vmcnt.
+    auto gather_index = [&](int t) -> int {
+        return c.sidx[min(t, ntiles - 1) * kRows + 8 * c.wave + jp];
+    };
+    auto gather_row = [&](int t, int pidx, int q) {
+        const unsigned lim_t = t < ntiles ? lim : 0u;
+        const unsigned p = (unsigned)__builtin_amdgcn_readlane(pidx, 8 * q);
+        const unsigned soff = p < lim_t ? p << 10 : kOutOfRange;
+        const int row = 8 * c.wave + q;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // keep the per-row lane offsets out of the loop
+        const unsigned voff = ((unsigned)(ln ^ lat_swz(row)) << 4) + soff;
+        load_lds16(c.kv_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + row * 1024, voff);
+    };
+    auto gather_pe = [&](int t, int pidx) {
+        const unsigned lim_t = t < ntiles ? lim : 0u;
+        const unsigned off = (unsigned)pidx < lim_t ? (unsigned)pidx * 128u + pe_lane : kOutOfRange;
+        load_lds16(c.pe_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + kLatBytes + c.wave * kPeBlock,
+                   off);
+    };
+    auto gather_tile = [&](int t) {
+        const int pidx = gather_index(t);
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-    l_run = 0.f;
-    gather_tile(c, 0);
-    if (ntiles > 1) gather_tile(c, 1);
-    if (ntiles > 2) gather_tile(c, 2);
+        for (int q = 0; q < 8; ++q) gather_row(t, pidx, q);
+        gather_pe(t, pidx);
+    };
 
-    for (int t = 0; t < ntiles; ++t) {
-        // own gathers of tile t done (9 loads per tile; later tiles may stay in flight)
-        const int ahead = min(ntiles - 1 - t, 2);
-        if (ahead >= 2) MLA_WAIT_VMCNT(18);
-        else if (ahead == 1) MLA_WAIT_VMCNT(9);
-        else MLA_WAIT_VMCNT(0);
-        __builtin_amdgcn_s_barrier();   // every wave's gathers of t landed; t-1 fully read
-        if (t + 3 < ntiles) gather_tile(c, t + 3);
-
-        // Per-tile bases (buffer offset folded in before the XOR, which keeps
-        // the swizzled addresses from being hoisted as loop invariants).
+    // Score operand (A) for k-step ks of the tile in buffer offset bo.
+    auto sc_read = [&](int bo, int ks) -> bf16x8 {
+        if (ks < 32)
+            return *(const __attribute__((address_space(3))) bf16x8*)(
+                tiles + (((sc_base + bo) ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+        return *(const __attribute__((address_space(3))) bf16x8*)(tiles + ((pe_base + bo) ^ ((ks - 32) << 5)));
+    };
+    // Standalone score chain (first tile).
+    auto scores = [&](int t, f32x16& out) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
-        const lds_u8* buf = (const lds_u8*)c.tiles;
-        const int sc_t = sc_base + bo, pe_t = pe_base + bo;
-        const int tr_t[2][2] = {{tr_base[0][0] + bo, tr_base[0][1] + bo}, {tr_base[1][0] + bo, tr_base[1][1] + bo}};
-        const int pv = c.sidx[t * kRows + j];
-        const unsigned vmask =
-            (unsigned)__builtin_amdgcn_ballot_w64(pv >= 0 && pv < c.T && pv <= c.limit);
-
-        // ---- scores S^T (rows x heads), accumulated in ordinary VGPRs.  The
-        // asm MFMAs keep their order, so operands are read four MFMAs ahead.
-        auto sc_read = [&](int ks) -> bf16x8 {
-            if (ks < 32)
-                return *(const __attribute__((address_space(3))) bf16x8*)(
-                    buf + ((sc_t ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
-            return *(const __attribute__((address_space(3))) bf16x8*)(buf + (pe_t ^ ((ks - 32) << 5)));
-        };
-        bf16x8 pre[4] = {sc_read(0), sc_read(1), sc_read(2), sc_read(3)};
         f32x16 sacc;
+        bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
             const bf16x8 av = pre[ks & 3];
-            if (ks + 4 < 36) pre[ks & 3] = sc_read(ks + 4);
+            if (ks + 4 < 36) pre[ks & 3] = sc_read(bo, ks + 4);
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
-            else mfma32_v(sacc, av, qf[ks]);
+            else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
+            else mfma32_v_last(out, sacc, av, qf[ks]);
         }
-        mfma_settle(sacc);
-        // validity of this lane's rows 8*(i/4) + 4*hsel + i%4
-        const unsigned vml = vmask >> (4 * hsel);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bool ok = (vml >> (8 * (i >> 2) + (i & 3))) & 1u;
-            sacc[i] = ok ? sacc[i] * c.a->scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sacc[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (m_ref == -INFINITY) m_ref = mx;   // nothing accumulated for this head yet
-        else if (mx > m_ref + 32.f) beaten = true;
+    };
 
-        // ---- probabilities p = 2^(s - m_ref) <= 2^32, as bf16 B operands
-        bf16x8 pb[2];
-        float psum = 0.f;
+    // Softmax bookkeeping of tile t, before its exponentials: mask the slots
+    // that are not selected (only in partial tiles) and take the reference
+    // from the first tile with a selected slot.  Returns the score multiplier
+    // to use (1 once masking has applied the scale).
+    bool have_ref = false;
+    auto prepare = [&](int t, f32x16& s) -> float {
+        const int pv = c.sidx[t * kRows + j];
+        const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64((unsigned)pv < lim);
+        float sc = c.a->scale_log2;
+        if (vmask != 0xFFFFFFFFu) {
+            // this lane's rows are 8*(i/4) + 4*hsel + i%4
+            const unsigned vml = vmask >> (4 * hsel);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = (sacc[i] == -INFINITY) ? 0.f : exp2f(sacc[i] - m_ref);
-            psum += p;
-            pb[i >> 3][i & 7] = (__bf16)p;
+            for (int i = 0; i < 16; ++i) {
+                const bool ok = (vml >> (8 * (i >> 2) + (i & 3))) & 1u;
+                s[i] = ok ? s[i] * sc : -INFINITY;
+            }
+            sc = 1.f;
         }
+        if (!have_ref && vmask != 0u) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i] * sc);
+            m_ref = fmaxf(mx, __shfl_xor(mx, 32));   // a head spans lanes l and l ^ 32
+            have_ref = true;
+        }
+        return sc;
+    };
+    // Probability of element i: 2^(s*sc - m_ref), into the bf16 B operand.
+    auto prob = [&](const f32x16& s, int i, float sc, float neg_m, bf16x8 (&pb)[2], float& psum) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sc, neg_m));
+        psum += p;
+        pb[i >> 3][i & 7] = (__bf16)p;
+    };
+    auto close_sum = [&](float psum) {
         l_run += psum;
+        beaten = beaten || !(psum <= kBeatenSum);
+    };
 
-        // ---- mix: O~^T[c][h] += V^T[c][j] P^T[j][h]; V^T fragments read three
-        // MFMAs ahead
+    // Mix: O~^T[c][h] += V^T[c][j] P^T[j][h]; V^T fragments read three MFMAs ahead.
+    auto mix = [&](int t, const bf16x8 (&pb)[2]) {
+        const int bo = (t & (kBufs - 1)) * kBufBytes;
+        const int tr_t[2][2] = {{tr_base[0][0] + bo, tr_base[0][1] + bo},
+                                {tr_base[1][0] + bo, tr_base[1][1] + bo}};
         auto tr_read = [&](int m) -> bf16x8 {
             const int cb = m >> 1, kc = m & 1;
             const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
-            return cat(lds_read_tr(buf + ((tr_t[kc][0] ^ x) + y)), lds_read_tr(buf + ((tr_t[kc][1] ^ x) + y)));
+            return cat(lds_read_tr(tiles + ((tr_t[kc][0] ^ x) + y)),
+                       lds_read_tr(tiles + ((tr_t[kc][1] ^ x) + y)));
         };
         bf16x8 vpre[3] = {tr_read(0), tr_read(1), tr_read(2)};
 #pragma unroll
@@ -398,11 +424,71 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             if (m + 3 < 32) vpre[m % 3] = tr_read(m + 3);
             acc[m >> 1] = mfma32(av, pb[m & 1], acc[m >> 1]);
         }
+    };
+
+    // Iteration t with a next tile: scores of t+1 into snext, softmax of t
+    // from scur, gather of t+3, then the mix of t.
+    auto body = [&](int t, f32x16& scur, f32x16& snext) {
+        const float sc = prepare(t, scur);
+        const float neg_m = have_ref ? -m_ref : 0.f;
+        MLA_WAIT_VMCNT(9);               // own gathers of t+1 done (t+2 may stay in flight)
+        __builtin_amdgcn_s_barrier();    // all of t+1 landed; every wave is done with t-1
+        const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
+        const int pidx = gather_index(t + 3);
+        bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
+        bf16x8 pb[2];
+        float psum = 0.f;
+        f32x16 sacc;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8 av = pre[ks & 3];
+            if (ks + 4 < 36) pre[ks & 3] = sc_read(bo, ks + 4);
+            if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
+            else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
+            else mfma32_v_last(snext, sacc, av, qf[ks]);
+            if (ks < 16) prob(scur, ks, sc, neg_m, pb, psum);
+            if (ks == 16) close_sum(psum);
+            if (ks >= 18 && ks < 26) gather_row(t + 3, pidx, ks - 18);
+            if (ks == 26) gather_pe(t + 3, pidx);
+        }
+        mix(t, pb);
+    };
+    // Last tile: softmax and mix only.
+    auto last = [&](int t, f32x16& scur) {
+        const float sc = prepare(t, scur);
+        const float neg_m = have_ref ? -m_ref : 0.f;
+        bf16x8 pb[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) prob(scur, i, sc, neg_m, pb, psum);
+        close_sum(psum);
+        mix(t, pb);
+    };
+
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
+    l_run = 0.f;
+    gather_tile(0);
+    gather_tile(1);
+    gather_tile(2);
+    MLA_WAIT_VMCNT(18);                  // own gathers of tile 0 done
+    __builtin_amdgcn_s_barrier();
+    f32x16 sA, sB;
+    scores(0, sA);
+    int t = 0;
+    for (; t + 1 < ntiles; ++t) {
+        body(t, sA, sB);
+        sA = sB;
     }
-    MLA_WAIT_VMCNT(0);
+    last(t, sA);
+    MLA_WAIT_VMCNT(0);                   // no gather may land after the workgroup ends
 }
 
-// Write this split's normalised bf16 mix (+ reference and sum when split).
+// Write this split's normalised bf16 mix (+ reference and sum).  Each wave
+// stages its 32 head rows in LDS (the tile buffers are free by now) and then
+// writes every row with one 1 KiB store instruction.
+constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (spreads banks)
+
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
                                             float l_run, bool beaten) {
     const AttnArgs& a = *c.a;
@@ -411,15 +497,29 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h = 32 * c.wave + (lane & 31);
     const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h;
-    __bf16* dst = reinterpret_cast<__bf16*>(a.o) + orow * kLatent + 4 * (lane >> 5);
+
+    // This lane holds columns 32cb + 8gq + 4(lane/32) .. +3 of head h.
+    __syncthreads();                                     // every wave is done with the tiles
+    unsigned char* stage = c.tiles + c.wave * (32 * kOutRow);
+    unsigned char* mine = stage + (lane & 31) * kOutRow + 8 * (lane >> 5);
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq)
-            *reinterpret_cast<bf16x4*>(dst + 32 * cb + 8 * gq) =
+            *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
                 to_bf16x4(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv, acc[cb][4 * gq + 2] * inv,
                           acc[cb][4 * gq + 3] * inv);
-    // A head whose reference was beaten by more than 32 is marked with a
+    // the wave reads back only its own rows: no workgroup barrier needed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
+#pragma unroll 8
+    for (int row = 0; row < 32; ++row) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOutRow + 16 * lane);
+        *reinterpret_cast<u32x4*>(dst0 + (size_t)row * kLatent + 8 * lane) = v;
+    }
+    // A head whose probabilities outgrew its reference is marked with a
     // negative sum; the merge recomputes it exactly.
     beaten = beaten || __shfl_xor((int)beaten, 32);
     if (lane < 32) {
@@ -481,46 +581,27 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
 // out^T = W_UV[h] . O~^T, so W_UV rows (d) are the A operand, loaded straight
 // from HBM with 16-byte reads (c is contiguous in the weight).  Workgroup =
 // (head, group of 32-row query blocks); wave w owns 32 values d and keeps its
-// W_UV slice (32 x 512) in registers.  Each 32-row block of O~ is staged in
-// LDS as bf16 once per workgroup: copied when the index list was not split,
-// else merged from the split partials.
+// W_UV slice (32 x 512) in registers.
+// Each 32-row block of O~ is built in LDS: the split partials of up to four
+// splits at a time are loaded straight into LDS (latent chunk c of row j at
+// the same swizzled position as in the attention tiles), merged in float32
+// with weights w_s = l_s 2^(m_s - max) / sum, and written back as bf16 into
+// the first split's rows, which then feed the MFMA B operand.
 // --------------------------------------------------------------------------
-constexpr int kORow = 1040;   // bytes per staged O~ row (512 bf16 + pad)
+constexpr int kUvRows = 32;
+constexpr int kUvGroup = 4;                    // splits staged in LDS at a time
+constexpr int kUvStage = kUvGroup * kUvRows * 1024;
 
-// Merge the split partials of one (query row, head), 8 columns starting at 8*ch.
-// Split s holds its normalised mix O~_s (bf16), its running max m_s (log2
-// domain) and its probability sum l_s; the merged row is
-// sum_s w_s O~_s / sum_s w_s with w_s = l_s * 2^(m_s - max_s m_s).
-__device__ __forceinline__ bf16x8 merge_partials(const __bf16* o_part, const float* m_part,
-                                                 const float* l_part, int R, int n_split, int rr,
-                                                 int h, int ch) {
-    float mmax = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp) mmax = fmaxf(mmax, m_part[((size_t)sp * R + rr) * kHeads + h]);
-    float W = 0.f;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (mmax != -INFINITY) {
-        for (int sp = 0; sp < n_split; ++sp) {
-            const size_t o = ((size_t)sp * R + rr) * kHeads + h;
-            const float ls = l_part[o];
-            if (!(ls > 0.f)) continue;
-            const float wgt = ls * exp2f(m_part[o] - mmax);
-            W += wgt;
-            const bf16x8 v = *reinterpret_cast<const bf16x8*>(o_part + o * kLatent + 8 * ch);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] += wgt * (float)v[q];
-        }
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    bf16x8 v;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = (__bf16)(x[q] * inv);
-    return v;
+// LDS byte offset of bf16 column col of staged row j (16-byte chunk swizzle).
+__device__ __forceinline__ int uv_pos(int j, int col) {
+    const int c8 = col >> 3;
+    return j * 1024 + (((c8 & ~15) | ((c8 & 15) ^ lat_swz(j))) << 4) + ((col & 7) << 1);
 }
 
 // Exact mix of one (query row, head) in float32, for a head whose first-tile
-// reference was beaten by more than 2^32 during the attention pass: pass one
-// finds the maximum score over the row's whole index list, pass two weighs and
-// mixes the selected latent rows (one 256-slot chunk at a time).  The result,
+// reference was beaten during the attention pass: pass one finds the maximum
+// score over the row's whole index list, pass two weighs and mixes the
+// selected latent rows (one 256-slot chunk at a time).  The result,
 // normalised, is written to out[0..511].  All 256 threads take part.
 __device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* red, float* p_s,
                           int* pos_s) {
@@ -579,24 +660,50 @@ __device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* r
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
-                                               __bf16* __restrict__ out, int r_groups) {
-    __shared__ __attribute__((aligned(16))) unsigned char obuf[32 * kORow];
+__global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
+                                                  __bf16* __restrict__ out, int r_groups) {
+    __shared__ __attribute__((aligned(1024))) unsigned char stage[kUvStage];
+    __shared__ float s_mmax[kUvRows], s_inv[kUvRows];
+    __shared__ float s_w[kUvGroup][kUvRows];
+    __shared__ int marked[kUvRows];
     __shared__ float xo[kLatent];
     __shared__ float xred[4];
     __shared__ float xp[256];
     __shared__ int xpos[256];
-    __shared__ int marked[32];
-    const void* o_ws = a.o;
-    const float* m_part = a.m_part;
-    const float* l_part = a.l_part;
     const int R = a.R;
     const int n_split = a.n_split;
     const int h = blockIdx.x;
+    const int tid = threadIdx.x;
     const int wave = wave_id();
-    const int lane = threadIdx.x & 63;
+    const int lane = tid & 63;
     const int half = lane >> 5;
     const int d = 32 * wave + (lane & 31);
+    const unsigned stage_addr = (unsigned)(size_t)stage;
+    const __bf16* o_ws = reinterpret_cast<const __bf16*>(a.o);
+
+    // Partial rows (split g0 + wave, query row rb*32 + j) -> staged row
+    // (wave, j); rows past R or splits past n_split load zeros.
+    auto stage_group = [&](int rb, int g0) {
+        const int sp = g0 + wave;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll 4
+        for (int j = 0; j < kUvRows; ++j) {
+            const int rr = rb * kUvRows + j;
+            const bool ok = rr < R && sp < n_split;
+            const __bf16* src = o_ws + (((size_t)(ok ? sp : 0) * R + (ok ? rr : 0)) * kHeads + h) * kLatent;
+            const u32x4 desc = make_desc(src, ok ? 1024u : 0u);
+            const unsigned voff = (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(j))) << 4);
+            load_lds16(desc, stage_addr + (wave * kUvRows + j) * 1024, voff);
+        }
+    };
+    // Merge weight of a split with reference m and sum l for a row with
+    // maximum mm and inverse weight sum inv: l 2^(m - mm) inv; a split with no
+    // selected slot (l = 0) or an inexact one (l < 0) weighs 0.
+    auto weight = [&](float m, float l, float mm, float inv) {
+        const float w = n_split == 1 ? 1.f : l * exp2f(m - mm) * inv;
+        return l > 0.f ? w : 0.f;
+    };
 
     bf16x8 wa[32];
     {
@@ -605,56 +712,117 @@ __global__ __launch_bounds__(256) void uv_bf16(AttnArgs a, const __bf16* __restr
         for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
     }
 
-    for (int rb = blockIdx.y; rb * 32 < R; rb += r_groups) {
-        // stage O~ rows rb*32 .. +31 of head h: 32 rows x 64 chunks of 8 columns
-        if (n_split == 1) {
-            u32x4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = threadIdx.x + 256 * i;
-                const int rr = rb * 32 + (e >> 6);
-                v[i] = rr < R ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(o_ws) +
-                                                                 ((size_t)rr * kHeads + h) * kLatent + 8 * (e & 63))
-                              : u32x4{0u, 0u, 0u, 0u};
+    // merge lanes: thread -> staged row mj, chunks mp[i] = 8i + (tid % 8), with
+    // the 8-chunk groups of odd rows rotated to spread LDS banks
+    const int mj = tid >> 3;
+    const int msub = tid & 7;
+
+    for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups) {
+        stage_group(rb, 0);
+        // per-row maximum, inverse weight sum and inexact flag over all splits;
+        // lanes mj*8 .. mj*8+7 share row mj, lane msub takes splits msub + 8i
+        {
+            const int rr = rb * kUvRows + mj;
+            float mloc = -INFINITY, wloc = 0.f, m0 = -INFINITY, l0 = 0.f;
+            int bad = 0;
+            if (rr < R) {
+                for (int sp = msub; sp < n_split; sp += 8) {
+                    const size_t o = ((size_t)sp * R + rr) * kHeads + h;
+                    const float l = a.l_part[o];
+                    const float m = a.m_part[o];
+                    if (sp == msub) {
+                        m0 = m;
+                        l0 = l;
+                    }
+                    bad |= l < 0.f;
+                    const bool ok = l > 0.f;
+                    const float mn = ok ? fmaxf(mloc, m) : mloc;
+                    wloc = (wloc > 0.f ? wloc * exp2f(mloc - mn) : 0.f) + (ok ? l * exp2f(m - mn) : 0.f);
+                    mloc = mn;
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = threadIdx.x + 256 * i;
-                *reinterpret_cast<u32x4*>(obuf + (e >> 6) * kORow + 16 * (e & 63)) = v[i];
+            for (int o = 1; o < 8; o <<= 1) {
+                const float m2 = __shfl_xor(mloc, o);
+                const float w2 = __shfl_xor(wloc, o);
+                const float mx = fmaxf(mloc, m2);
+                wloc = (wloc > 0.f ? wloc * exp2f(mloc - mx) : 0.f) + (w2 > 0.f ? w2 * exp2f(m2 - mx) : 0.f);
+                mloc = mx;
+                bad |= __shfl_xor(bad, o);
             }
-        } else {
-            for (int e = threadIdx.x; e < 32 * 64; e += 256) {
-                const int rr = rb * 32 + (e >> 6);
-                const bf16x8 v = rr < R ? merge_partials(reinterpret_cast<const __bf16*>(o_ws), m_part,
-                                                         l_part, R, n_split, rr, h, e & 63)
-                                        : bf16x8{};
-                *reinterpret_cast<bf16x8*>(obuf + (e >> 6) * kORow + 16 * (e & 63)) = v;
+            const float inv = wloc > 0.f ? 1.f / wloc : 0.f;
+            if (msub == 0) {
+                s_mmax[mj] = mloc;
+                s_inv[mj] = inv;
+                marked[mj] = bad;
+            }
+            // weights of the first staged group come from the values at hand
+            if (msub < kUvGroup) s_w[msub][mj] = (rr < R && msub < n_split) ? weight(m0, l0, mloc, inv) : 0.f;
+        }
+        float x[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+
+        for (int g0 = 0; g0 < n_split; g0 += kUvGroup) {
+            if (g0 > 0) {
+                __syncthreads();             // previous group fully read
+                stage_group(rb, g0);
+                if (tid < kUvGroup * kUvRows) {
+                    const int sl = tid >> 5, j = tid & 31;
+                    const int rr = rb * kUvRows + j;
+                    float w = 0.f;
+                    if (rr < R && g0 + sl < n_split) {
+                        const size_t o = ((size_t)(g0 + sl) * R + rr) * kHeads + h;
+                        w = weight(a.m_part[o], a.l_part[o], s_mmax[j], s_inv[j]);
+                    }
+                    s_w[sl][j] = w;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // own partial rows landed
+            __syncthreads();                 // all rows and weights visible
+            const int gn = min(kUvGroup, n_split - g0);
+            for (int sl = 0; sl < gn; ++sl) {
+                const float w = s_w[sl][mj];
+                if (w == 0.f) continue;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int pos = (8 * i + msub) ^ ((mj & 1) << 3);
+                    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + (sl * kUvRows + mj) * 1024 + pos * 16);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[i][e] += w * (float)v[e];
+                }
             }
         }
-        // heads whose attention pass was marked inexact: recompute exactly
-        if (threadIdx.x < 32) {
-            const int rr = rb * 32 + threadIdx.x;
-            int bad = 0;
-            if (rr < R)
-                for (int sp = 0; sp < n_split; ++sp) bad |= l_part[((size_t)sp * R + rr) * kHeads + h] < 0.f;
-            marked[threadIdx.x] = bad;
+        __syncthreads();                     // every staged row read
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pos = (8 * i + msub) ^ ((mj & 1) << 3);
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[i][e];
+            *reinterpret_cast<bf16x8*>(stage + mj * 1024 + pos * 16) = v;
         }
         __syncthreads();
-        for (int row = 0; row < 32; ++row) {
+        // heads whose attention pass was marked inexact: recompute exactly
+        for (int row = 0; row < kUvRows; ++row) {
             if (!marked[row]) continue;
-            exact_mix(a, rb * 32 + row, h, xo, xred, xp, xpos);
-            for (int c = threadIdx.x; c < kLatent; c += 256)
-                *reinterpret_cast<__bf16*>(obuf + row * kORow + 2 * c) = (__bf16)xo[c];
+            exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
+            for (int c = tid; c < kLatent; c += 256)
+                *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
             __syncthreads();
         }
+        // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
+        const int j = lane & 31;
+        const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
         f32x16 acc = {};
-        const unsigned char* brow = obuf + (lane & 31) * kORow + 16 * half;
 #pragma unroll
         for (int ks = 0; ks < 32; ++ks) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + 32 * ks);
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(stage + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
             acc = mfma32(wa[ks], bv, acc);
         }
-        const int r = rb * 32 + (lane & 31);
+        const int r = rb * kUvRows + j;
         if (r < R) {
             __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
 #pragma unroll
@@ -662,7 +830,7 @@ __global__ __launch_bounds__(256) void uv_bf16(AttnArgs a, const __bf16* __restr
                 *reinterpret_cast<bf16x4*>(dst + 8 * g) =
                     to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
         }
-        __syncthreads();
+        __syncthreads();                     // staging reused by the next block
     }
 }
 
