@@ -104,9 +104,13 @@ __device__ __forceinline__ int wave_id() {
 // query row.  Workgroup = (head, quarter of c, group of 32-row query blocks).
 // The weight slice [128 d x 128 c] is staged in LDS with 16-byte loads and
 // read back transposed; wave w keeps the fragments of its 32 columns in
-// registers for every query block it visits.
+// registers for every query block it visits.  The first block's queries are
+// loaded together with the weight (one memory round trip), and each output
+// block goes through LDS so that every row segment (128 c = 256 bytes) is
+// written by 16 consecutive lanes.
 // --------------------------------------------------------------------------
 constexpr int kWRow = 320;   // bytes per staged W_UK row (128 bf16 + pad)
+constexpr int kQcRow = 272;  // bytes per staged output row (128 bf16 + pad)
 
 __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ q_nope,
                                                      const __bf16* __restrict__ q_pe,
@@ -114,11 +118,26 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
                                                      __bf16* __restrict__ q_out, int R,
                                                      int r_groups) {
     __shared__ __attribute__((aligned(16))) unsigned char wbuf[kNope * kWRow];
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[32 * kQcRow];
     const int h = blockIdx.x >> 2;
     const int cq = blockIdx.x & 3;
+    const int tid = threadIdx.x;
     const int wave = wave_id();
-    const int lane = threadIdx.x & 63;
+    const int lane = tid & 63;
     const int half = lane >> 5;
+
+    // B fragments of one 32-row block: q_nope[r][h][16ks + 8half .. +7], r = lane % 32
+    auto load_q = [&](int rb, bf16x8 (&b)[8]) {
+        const int r = rb * 32 + (lane & 31);
+        const bool rv = r < R;
+        const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) b[ks] = rv ? *reinterpret_cast<const bf16x8*>(qn + 16 * ks) : bf16x8{};
+    };
+    const int blocks = (R + 31) / 32;
+    bf16x8 b0[8], b1[8];
+    load_q(blockIdx.y, b0);
+    if (blockIdx.y + r_groups < blocks) load_q(blockIdx.y + r_groups, b1);
 
     {
         // 128 rows d x 16 chunks of 8 columns; 8 chunks per thread
@@ -126,12 +145,12 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
         u32x4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int e = threadIdx.x + 256 * i;
+            const int e = tid + 256 * i;
             v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)(e >> 4) * kLatent + 8 * (e & 15));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int e = threadIdx.x + 256 * i;
+            const int e = tid + 256 * i;
             *reinterpret_cast<u32x4*>(wbuf + (e >> 4) * kWRow + 16 * (e & 15)) = v[i];
         }
     }
@@ -149,32 +168,44 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
             a[ks] = cat(lds_read_tr(base + 16 * ks * kWRow), lds_read_tr(base + (16 * ks + 4) * kWRow));
     }
 
-    const int c_base = cq * 128 + wave * 32;
-    for (int rb = blockIdx.y; rb * 32 < R; rb += r_groups) {
-        const int r = rb * 32 + (lane & 31);
-        const bool rv = r < R;
+    auto process = [&](int rb, const bf16x8 (&b)[8]) {
         f32x16 acc = {};
-        const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 8 * half;
-        bf16x8 b[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) b[ks] = rv ? *reinterpret_cast<const bf16x8*>(qn + 16 * ks) : bf16x8{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], b[ks], acc);
-        if (rv) {
-            __bf16* dst = q_out + ((size_t)r * kHeads + h) * kQRow + c_base + 4 * half;
+        // lane holds c = 32*wave + 8g + 4*half .. +3 of row lane % 32
+        unsigned char* mine = obuf + (lane & 31) * kQcRow + (32 * wave + 4 * half) * 2;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
-                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<bf16x4*>(mine + 16 * g) =
+                to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        __syncthreads();
+        // 32 rows x 16 chunks of 16 bytes: two chunks per thread
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + 256 * i;
+            const int rr = rb * 32 + (e >> 4);
+            if (rr < R)
+                *reinterpret_cast<u32x4*>(q_out + ((size_t)rr * kHeads + h) * kQRow + cq * 128 + 8 * (e & 15)) =
+                    *reinterpret_cast<const u32x4*>(obuf + (e >> 4) * kQcRow + 16 * (e & 15));
         }
         if (cq == 0) {
             // q_pe rows of this block: 32 rows x 8 chunks of 16 bytes = one per thread.
-            const int rr = rb * 32 + (threadIdx.x >> 3);
-            const int ch = threadIdx.x & 7;
+            const int rr = rb * 32 + (tid >> 3);
+            const int ch = tid & 7;
             if (rr < R) {
                 *reinterpret_cast<bf16x8*>(q_out + ((size_t)rr * kHeads + h) * kQRow + kLatent + 8 * ch) =
                     *reinterpret_cast<const bf16x8*>(q_pe + ((size_t)rr * kHeads + h) * kRope + 8 * ch);
             }
+        }
+        __syncthreads();                  // obuf reused by the next block
+    };
+    // Two query blocks in flight: while one is multiplied, the next but one loads.
+    for (int rb = blockIdx.y; rb < blocks; rb += 2 * r_groups) {
+        process(rb, b0);
+        if (rb + 2 * r_groups < blocks) load_q(rb + 2 * r_groups, b0);
+        if (rb + r_groups < blocks) {
+            process(rb + r_groups, b1);
+            if (rb + 3 * r_groups < blocks) load_q(rb + 3 * r_groups, b1);
         }
     }
 }
@@ -215,6 +246,17 @@ constexpr int kBufs = 4;                     // tile buffers
 constexpr int kLatBytes = kRows * 1024;
 constexpr int kPeBlock = 1152;               // 8 rotary rows (1 KiB) + 128-byte pad
 constexpr int kBufBytes = kLatBytes + 4 * kPeBlock;
+constexpr int kPRow = 80;                    // P^T staging row: 32 bf16 + 16-byte pad (one head)
+
+// Workgroup barrier after this wave's LDS writes have completed.  Written as
+// assembly with a memory clobber so that the compiler keeps LDS accesses on
+// their side of it; global loads in flight (the gathers) are not waited for.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("s_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -242,16 +284,52 @@ __device__ __forceinline__ void load_lds16(u32x4 rsrc, unsigned lds_addr, unsign
         : "memory");
 }
 
+// Four such loads into the LDS rows lds_addr, +1 KiB, +2 KiB, +3 KiB with a
+// single M0 value: the instruction offset (0, 1024, 2048, 3072) moves both the
+// LDS destination and the memory address, so each memory offset passed in is
+// its true offset + 3072 - 1024*u, against a descriptor whose base sits 3 KiB
+// before the data (see make_desc_x4).  Rewriting M0 before every load would
+// hold each load until the previous one has landed, which caps a wave at one
+// load in flight; this way four are.
+constexpr unsigned kX4Bias = 3072u;
+__device__ __forceinline__ void load_lds16_x4(u32x4 rsrc, unsigned lds_addr, unsigned v0, unsigned v1,
+                                              unsigned v2, unsigned v3) {
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc)
+        : "memory");
+}
+// Offset for lane data at true offset `off` of load u of a group (or out of range).
+__device__ __forceinline__ unsigned x4_off(bool ok, unsigned off, int u) {
+    return ok ? off + kX4Bias - 1024u * (unsigned)u : kOutOfRange;
+}
+
 // Raw buffer descriptor (stride 0) over `bytes` bytes at `base`.
 __device__ __forceinline__ u32x4 make_desc(const void* base, unsigned bytes) {
     const unsigned long long b = reinterpret_cast<unsigned long long>(base);
     return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+// Descriptor for load_lds16_x4 over `bytes` bytes at `base`: it starts kX4Bias
+// bytes early and covers them too (the loads never touch that prefix).
+__device__ __forceinline__ u32x4 make_desc_x4(const void* base, unsigned bytes) {
+    const unsigned long long b = reinterpret_cast<unsigned long long>(base) - kX4Bias;
+    return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, bytes + kX4Bias, 0x00020000u};
 }
 
 // Everything one workgroup needs to process one (query row, split).
 struct SplitCtx {
     const AttnArgs* a;
     unsigned char* tiles;        // kBufs tile buffers in LDS (generic pointer to LDS)
+    unsigned char* pbuf;         // probabilities of one tile, [head][slot order], kPRow per head
     const int* sidx;             // the split's index list in LDS (-1 past its end)
     const __bf16* qrow;          // this lane's absorbed-query row, offset to its k half
     u32x4 kv_desc, pe_desc;
@@ -322,15 +400,21 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     auto gather_index = [&](int t) -> int {
         return c.sidx[min(t, ntiles - 1) * kRows + 8 * c.wave + jp];
     };
-    auto gather_row = [&](int t, int pidx, int q) {
+    // latent rows 8*wave + 4*g .. +3 of tile t (one M0 value for the four)
+    auto gather_rows4 = [&](int t, int pidx, int g) {
         const unsigned lim_t = t < ntiles ? lim : 0u;
-        const unsigned p = (unsigned)__builtin_amdgcn_readlane(pidx, 8 * q);
-        const unsigned soff = p < lim_t ? p << 10 : kOutOfRange;
-        const int row = 8 * c.wave + q;
         int ln = lane;
         asm volatile("" : "+v"(ln));   // keep the per-row lane offsets out of the loop
-        const unsigned voff = ((unsigned)(ln ^ lat_swz(row)) << 4) + soff;
-        load_lds16(c.kv_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + row * 1024, voff);
+        unsigned v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = 4 * g + u;
+            const unsigned p = (unsigned)__builtin_amdgcn_readlane(pidx, 8 * q);
+            const int row = 8 * c.wave + q;
+            v[u] = x4_off(p < lim_t, (p << 10) + ((unsigned)(ln ^ lat_swz(row)) << 4), u);
+        }
+        load_lds16_x4(c.kv_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + (8 * c.wave + 4 * g) * 1024,
+                      v[0], v[1], v[2], v[3]);
     };
     auto gather_pe = [&](int t, int pidx) {
         const unsigned lim_t = t < ntiles ? lim : 0u;
@@ -340,8 +424,8 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     };
     auto gather_tile = [&](int t) {
         const int pidx = gather_index(t);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) gather_row(t, pidx, q);
+        gather_rows4(t, pidx, 0);
+        gather_rows4(t, pidx, 1);
         gather_pe(t, pidx);
     };
 
@@ -406,23 +490,51 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         beaten = beaten || !(psum <= kBeatenSum);
     };
 
-    // Mix: O~^T[c][h] += V^T[c][j] P^T[j][h]; V^T fragments read three MFMAs ahead.
-    auto mix = [&](int t, const bf16x8 (&pb)[2]) {
-        const int bo = (t & (kBufs - 1)) * kBufBytes;
-        const int tr_t[2][2] = {{tr_base[0][0] + bo, tr_base[0][1] + bo},
-                                {tr_base[1][0] + bo, tr_base[1][1] + bo}};
-        auto tr_read = [&](int m) -> bf16x8 {
-            const int cb = m >> 1, kc = m & 1;
-            const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
-            return cat(lds_read_tr(tiles + ((tr_t[kc][0] ^ x) + y)),
-                       lds_read_tr(tiles + ((tr_t[kc][1] ^ x) + y)));
-        };
-        bf16x8 vpre[3] = {tr_read(0), tr_read(1), tr_read(2)};
+    // The probabilities of a tile go through LDS: lane (head h, half g) holds
+    // rows 8a + 4g + b (a, b = 0..3), which sit in MFMA k slot 8g + 4(a%2) + b
+    // of k-step a/2 (the slot order of the transposing V reads below), so
+    // each lane writes four 8-byte runs and the mix reads 16 bytes per operand.
+    const lds_u8* pbuf = (const lds_u8*)c.pbuf;
+    auto store_p = [&](const bf16x8 (&pb)[2]) {
+        unsigned char* row = c.pbuf + (32 * c.wave + (lane & 31)) * kPRow + 16 * hsel;
 #pragma unroll
-        for (int m = 0; m < 32; ++m) {
-            const bf16x8 av = vpre[m % 3];
-            if (m + 3 < 32) vpre[m % 3] = tr_read(m + 3);
-            acc[m >> 1] = mfma32(av, pb[m & 1], acc[m >> 1]);
+        for (int a = 0; a < 4; ++a) {
+            const bf16x4 v = {pb[a >> 1][4 * (a & 1)], pb[a >> 1][4 * (a & 1) + 1],
+                              pb[a >> 1][4 * (a & 1) + 2], pb[a >> 1][4 * (a & 1) + 3]};
+            *reinterpret_cast<bf16x4*>(row + 32 * (a >> 1) + 8 * (a & 1)) = v;
+        }
+    };
+    // Mix of the wave's quarter of the latent columns for all 128 heads:
+    // O~^T[c][h] += V^T[c][j] P^T[j][h], c = 128*wave + 32*cbi + (0..31),
+    // h = 32*hb + (0..31); acc[4*cbi + hb].
+    auto mix = [&](int t, auto&& side) {
+        const int bo = (t & (kBufs - 1)) * kBufBytes;
+        const int y = c.wave * 256;
+        auto v_read = [&](int idx) -> bf16x8 {      // idx = 4*kc + cbi
+            const int kc = idx >> 2, x = (idx & 3) << 6;
+            return cat(lds_read_tr(tiles + (((tr_base[kc][0] + bo) ^ x) + y)),
+                       lds_read_tr(tiles + (((tr_base[kc][1] + bo) ^ x) + y)));
+        };
+        auto p_read = [&](int hb, int kc) -> bf16x8 {
+            return *(const __attribute__((address_space(3))) bf16x8*)(
+                pbuf + (32 * hb + (lane & 31)) * kPRow + 32 * kc + 16 * hsel);
+        };
+        bf16x8 pk[2][4];
+        bf16x8 va[2];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pk[0][hb] = p_read(hb, 0);
+        va[0] = v_read(0);
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx) {
+            if (idx + 1 < 8) va[(idx + 1) & 1] = v_read(idx + 1);
+            if (idx == 2)
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) pk[1][hb] = p_read(hb, 1);
+            const int kc = idx >> 2, cbi = idx & 3;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                acc[4 * cbi + hb] = mfma32(va[idx & 1], pk[kc][hb], acc[4 * cbi + hb]);
+            if (idx == 3) side();
         }
     };
 
@@ -432,7 +544,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         const float sc = prepare(t, scur);
         const float neg_m = have_ref ? -m_ref : 0.f;
         MLA_WAIT_VMCNT(9);               // own gathers of t+1 done (t+2 may stay in flight)
-        __builtin_amdgcn_s_barrier();    // all of t+1 landed; every wave is done with t-1
+        barrier_only();                  // all of t+1 landed; every wave is done with t-1 and P
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
         bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
@@ -448,10 +560,12 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             else mfma32_v_last(snext, sacc, av, qf[ks]);
             if (ks < 16) prob(scur, ks, sc, neg_m, pb, psum);
             if (ks == 16) close_sum(psum);
-            if (ks >= 18 && ks < 26) gather_row(t + 3, pidx, ks - 18);
-            if (ks == 26) gather_pe(t + 3, pidx);
+            if (ks == 17) store_p(pb);
+            if (ks == 18) gather_rows4(t + 3, pidx, 0);
+            if (ks == 26) gather_rows4(t + 3, pidx, 1);
         }
-        mix(t, pb);
+        barrier_lds();                   // every head's probabilities of tile t in LDS
+        mix(t, [&] { gather_pe(t + 3, pidx); });
     };
     // Last tile: softmax and mix only.
     auto last = [&](int t, f32x16& scur) {
@@ -462,7 +576,9 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 #pragma unroll
         for (int i = 0; i < 16; ++i) prob(scur, i, sc, neg_m, pb, psum);
         close_sum(psum);
-        mix(t, pb);
+        store_p(pb);
+        barrier_lds();
+        mix(t, [] {});
     };
 
 #pragma unroll
@@ -472,7 +588,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     gather_tile(1);
     gather_tile(2);
     MLA_WAIT_VMCNT(18);                  // own gathers of tile 0 done
-    __builtin_amdgcn_s_barrier();
+    barrier_only();
     f32x16 sA, sB;
     scores(0, sA);
     int t = 0;
@@ -485,8 +601,10 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 }
 
 // Write this split's normalised bf16 mix (+ reference and sum).  Each wave
-// stages its 32 head rows in LDS (the tile buffers are free by now) and then
-// writes every row with one 1 KiB store instruction.
+// holds a quarter of the columns of every head; the sums live with the waves
+// that computed the heads' scores, so they go through LDS first.  Rows are
+// staged in LDS (the tile buffers are free by now) and every head row is
+// written with one 1 KiB store instruction.
 constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (spreads banks)
 
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
@@ -494,26 +612,32 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     const AttnArgs& a = *c.a;
     const int lane = c.lane;
     const float l_tot = l_run + __shfl_xor(l_run, 32);   // a head spans lanes l and l ^ 32
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int h = 32 * c.wave + (lane & 31);
-    const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h;
+    const int h_own = 32 * c.wave + (lane & 31);
+    float* inv_l = reinterpret_cast<float*>(c.pbuf);
+    barrier_only();                                      // every wave is done with tiles and P
+    if (lane < 32) inv_l[h_own] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    barrier_lds();
+    float inv[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) inv[hb] = inv_l[32 * hb + (lane & 31)];
 
-    // This lane holds columns 32cb + 8gq + 4(lane/32) .. +3 of head h.
-    __syncthreads();                                     // every wave is done with the tiles
-    unsigned char* stage = c.tiles + c.wave * (32 * kOutRow);
-    unsigned char* mine = stage + (lane & 31) * kOutRow + 8 * (lane >> 5);
+    // acc[4*cbi + hb] element i: head 32hb + lane%32, column
+    // 128*wave + 32*cbi + 8*(i/4) + 4*(lane/32) + i%4.
+    unsigned char* mine = c.tiles + (lane & 31) * kOutRow + (128 * c.wave + 4 * (lane >> 5)) * 2;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+    for (int cbi = 0; cbi < 4; ++cbi)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-            *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
-                to_bf16x4(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv, acc[cb][4 * gq + 2] * inv,
-                          acc[cb][4 * gq + 3] * inv);
-    // the wave reads back only its own rows: no workgroup barrier needed
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x16& v = acc[4 * cbi + hb];
+                *reinterpret_cast<bf16x4*>(mine + 32 * hb * kOutRow + 64 * cbi + 16 * gq) =
+                    to_bf16x4(v[4 * gq] * inv[hb], v[4 * gq + 1] * inv[hb], v[4 * gq + 2] * inv[hb],
+                              v[4 * gq + 3] * inv[hb]);
+            }
+    barrier_lds();
     __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
+    const unsigned char* stage = c.tiles + 32 * c.wave * kOutRow;
 #pragma unroll 8
     for (int row = 0; row < 32; ++row) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOutRow + 16 * lane);
@@ -523,6 +647,7 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     // negative sum; the merge recomputes it exactly.
     beaten = beaten || __shfl_xor((int)beaten, 32);
     if (lane < 32) {
+        const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h_own;
         a.m_part[orow] = m_ref;
         a.l_part[orow] = beaten ? -1.f : l_tot;
     }
@@ -530,6 +655,7 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
 
 __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
     __shared__ __attribute__((aligned(1024))) unsigned char tiles[kBufs * kBufBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char pbuf[kHeads * kPRow];
     __shared__ int sidx[kMaxSlotsPerSplit];
 
     // Workgroup -> (query row, split).  Consecutive workgroups land on the 8
@@ -543,6 +669,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
     SplitCtx c;
     c.a = &a;
     c.tiles = tiles;
+    c.pbuf = pbuf;
     c.sidx = sidx;
     c.r = (a.R - 1) - rr;
     c.split = split;
@@ -553,7 +680,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
     c.ntiles = (nslots + kRows - 1) / kRows;
     c.limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + c.r;
     c.T = a.T;
-    c.kv_desc = make_desc(reinterpret_cast<const __bf16*>(a.kv) + (size_t)c.r * a.cache_rows_per_query * kLatent,
+    c.kv_desc = make_desc_x4(reinterpret_cast<const __bf16*>(a.kv) + (size_t)c.r * a.cache_rows_per_query * kLatent,
                           (unsigned)c.T * (kLatent * 2));
     c.pe_desc = make_desc(reinterpret_cast<const __bf16*>(a.pe) + (size_t)c.r * a.cache_rows_per_query * kRope,
                           (unsigned)c.T * (kRope * 2));
@@ -687,14 +814,21 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
         const int sp = g0 + wave;
         int ln = lane;
         asm volatile("" : "+v"(ln));
-#pragma unroll 4
-        for (int j = 0; j < kUvRows; ++j) {
-            const int rr = rb * kUvRows + j;
-            const bool ok = rr < R && sp < n_split;
-            const __bf16* src = o_ws + (((size_t)(ok ? sp : 0) * R + (ok ? rr : 0)) * kHeads + h) * kLatent;
-            const u32x4 desc = make_desc(src, ok ? 1024u : 0u);
-            const unsigned voff = (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(j))) << 4);
-            load_lds16(desc, stage_addr + (wave * kUvRows + j) * 1024, voff);
+        // rows j of split sp sit kHeads * kLatent bf16 apart in the workspace
+        const bool sp_ok = sp < n_split;
+        const __bf16* src0 = o_ws + (((size_t)(sp_ok ? sp : 0) * R + rb * kUvRows) * kHeads + h) * kLatent;
+        const unsigned row_bytes = kHeads * kLatent * 2;
+        const u32x4 desc = make_desc_x4(src0, sp_ok ? (unsigned)min(R - rb * kUvRows, kUvRows) * row_bytes : 0u);
+#pragma unroll 2
+        for (int j0 = 0; j0 < kUvRows; j0 += 4) {
+            unsigned v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u;
+                const bool ok = sp_ok && rb * kUvRows + j < R;
+                v[u] = x4_off(ok, (unsigned)j * row_bytes + (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(j))) << 4), u);
+            }
+            load_lds16_x4(desc, stage_addr + (wave * kUvRows + j0) * 1024, v[0], v[1], v[2], v[3]);
         }
     };
     // Merge weight of a split with reference m and sum l for a row with
@@ -838,8 +972,10 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
 
 hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
                               int R, hipStream_t s) {
+    // one workgroup per (head, quarter of c) and eight query blocks: the
+    // weight is read once per eight blocks
     const int blocks = (R + 31) / 32;
-    const int r_groups = blocks < 4 ? blocks : 4;
+    const int r_groups = (blocks + 7) / 8;
     hipLaunchKernelGGL(absorb_q_bf16, dim3(kHeads * 4, r_groups), dim3(256), 0, s,
                        static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_pe),
                        static_cast<const __bf16*>(w_uk), static_cast<__bf16*>(q_out), R, r_groups);

@@ -18,7 +18,7 @@ constexpr int kQRow = kLatent + kRope;  // 576: absorbed query row [q_c | q_pe]
 // split of that row's index list; splits hold whole tiles of kTileRows slots
 // and at most kMaxSlotsPerSplit slots.
 constexpr int kTileRows = 32;
-constexpr int kMaxSlotsPerSplit = 2048;
+constexpr int kMaxSlotsPerSplit = 1024;
 // Largest cache length: gathers address one query's cache with 32-bit byte
 // offsets that must stay below 2^31.
 constexpr int kMaxT = (1 << 21) - 1;
