@@ -330,7 +330,9 @@ struct SplitCtx {
     const AttnArgs* a;
     unsigned char* tiles;        // kBufs tile buffers in LDS (generic pointer to LDS)
     unsigned char* pbuf;         // probabilities of one tile, [head][slot order], kPRow per head
-    const int* sidx;             // the split's index list in LDS (-1 past its end)
+    int* sidx;                   // the split's index list in LDS (-1 past its end)
+    const int32_t* idx_src;      // the split's index list in global memory
+    int nslots;                  // its length
     const __bf16* qrow;          // this lane's absorbed-query row, offset to its k half
     u32x4 kv_desc, pe_desc;
     int r, split, ntiles, limit, T, wave, lane;
@@ -356,10 +358,25 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // Query fragments (B operands): head 32*wave + lane%32, columns
     // 16*ks + 8*(lane/32) .. +7.  Retiring their loads here leaves vmcnt
     // counting the gathers only inside the tile loop.
+    // Prologue, one memory round trip: the split's index list, the query
+    // fragments and (once the list is in LDS) the first three tiles are all in
+    // flight together.
+    constexpr int kIdxPerThread = kMaxSlotsPerSplit / 256;
+    int iv[kIdxPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        iv[u] = i < c.nslots ? c.idx_src[i] : -1;
+    }
     bf16x8 qf[36];
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 16 * ks);
-    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        if (i < ntiles * kRows) c.sidx[i] = iv[u];
+    }
+    barrier_lds();
 
     // Per-lane LDS offsets, relative to a tile buffer.  Buffer offsets are
     // multiples of 512 bytes, so XOR-ing a compile-time constant into bits 5..7
@@ -587,7 +604,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     gather_tile(0);
     gather_tile(1);
     gather_tile(2);
-    MLA_WAIT_VMCNT(18);                  // own gathers of tile 0 done
+    __builtin_amdgcn_s_waitcnt(0);       // query fragments and the first three tiles
     barrier_only();
     f32x16 sA, sB;
     scores(0, sA);
@@ -687,12 +704,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
     c.qrow = reinterpret_cast<const __bf16*>(a.q) +
              ((size_t)c.r * kHeads + 32 * c.wave + (c.lane & 31)) * kQRow + 8 * (c.lane >> 5);
 
-    // Index list of this split into LDS (-1 past its end).
-    {
-        const int32_t* src = a.idx + (size_t)c.r * a.k + slot_begin;
-        for (int i = threadIdx.x; i < c.ntiles * kRows; i += 256) sidx[i] = i < nslots ? src[i] : -1;
-    }
-    __syncthreads();
+    c.idx_src = a.idx + (size_t)c.r * a.k + slot_begin;
+    c.nslots = nslots;
 
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
