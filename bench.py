@@ -48,6 +48,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="batch rows timed on the CPU oracle (0 = size to ~15 s)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after the timed passes, run three plain device copies of this many MiB "
+                        "(the known-size kernel that scales the traffic counters)")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "this script with --copy-calibration-mib into " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    p.add_argument("--traffic-command", default="", help="command line recorded with --write-traffic")
     return p.parse_args()
 
 
@@ -95,6 +102,53 @@ def traffic_from_profile(launch_units: int):
     return rec.get("bytes_per_launch")
 
 
+def _counter_per_dispatch(out_dir: str, counter: str):
+    """[(dispatch id, kernel name, value summed over instances)] from a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {out_dir}")
+    acc = {}
+    for row in csv.DictReader(open(files[0])):
+        if row["Counter_Name"] != counter:
+            continue
+        key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+        acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    return [(d, n, v) for (d, n), v in sorted(acc.items())]
+
+
+def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int, command: str):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel by what the
+    same counters read for the calibration copy (copy_mib MiB read and written, the last
+    three copy dispatches of the run), and record the result next to the kernel's hash."""
+    units = 64 * 2048
+    known = copy_mib * 2 ** 20
+    rec = {"kernel_source_sha256_16": source_hash(),
+           "workload": "decode B=64 T=32768 k=2048, bf16 (bench.py defaults)",
+           "command": command, "calibration_copy_bytes": known}
+    for tag, d, counter in (("read", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_per_dispatch(d, counter)
+        attn = [v for _, n, v in rows if "attn_bf16" in n]
+        uv = [v for _, n, v in rows if "uv_bf16" in n]
+        absorb = [v for _, n, v in rows if "absorb_q_bf16" in n]
+        copies = [v for _, n, v in rows if "copyBuffer" in n][-3:]
+        if not attn or len(copies) < 3:
+            raise SystemExit(f"{d}: attention dispatches or calibration copies missing")
+        factor = known / (1024.0 * float(np.mean(copies)))
+        rec[f"{counter}_kib_attention"] = float(np.mean(attn))
+        rec[f"{counter}_kib_uv"] = float(np.mean(uv)) if uv else None
+        rec[f"{counter}_kib_absorb"] = float(np.mean(absorb)) if absorb else None
+        rec[f"{counter}_kib_calibration_copy"] = float(np.mean(copies))
+        rec[f"{tag}_scale"] = factor
+        rec[f"{tag}_bytes_per_launch"] = float(np.mean(attn)) * 1024.0 * factor
+    rec["bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    rec["algorithmic_bytes_per_launch"] = units * ROW_BYTES
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(cfg, rows_wanted: int):
     """Time the fp64 oracle on whole batch rows of the same workload (set 0)."""
     import oracle
@@ -129,6 +183,10 @@ def main():
               "(decode batch rows shard across GPUs with no exchange, so N GPUs run N copies "
               "of this one-GPU step)", file=sys.stderr)
         sys.exit(2)
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib,
+                      args.traffic_command)
+        return
 
     import torch
     import synth
@@ -254,6 +312,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
     print(json.dumps(result), flush=True)
