@@ -3,7 +3,7 @@
  *
  * The library computes DeepSeek-V3.2-Exp's sparse latent attention in its
  * absorbed form for 128 heads that share one latent cache ("Mix and project"
- * page, decode code model.py 590-606; "Key heads" page, Explanation: folding
+ * page, Explanation: the decode-branch code; "Key heads" page, Explanation: folding
  * W_UK into the query gives the same scores):
  *
  *   1. q_c[h]   = q_nope[h] . W_UK[h]                (512 per head)
@@ -84,7 +84,7 @@ MLA_API int mla_abi_version(void);
 
 /*
  * Decode: one new query per batch row against that row's cache.
- * ("Mix and project" page, decode code model.py 590-606: no causal mask, all
+ * ("Mix and project" page, Explanation, decode-branch code: no causal mask, all
  *  cached positions [0, T) are visible, the index mask keeps the top-k list.)
  *
  *   q_nope   [B, 128, 128]   q_pe [B, 128, 64] (already rotated)
@@ -111,7 +111,7 @@ MLA_API mla_status mla_sparse_decode(const void* q_nope, const void* q_pe,
  * Prefill chunk in latent form: S consecutive queries of ONE sequence against
  * its cache.  Query s sits at absolute position start_pos + s and ignores any
  * listed position greater than that (the causal mask the model adds in its
- * prefill branch, "Key heads" page, code model.py 574-589).
+ * prefill branch, "Key heads" page, Explanation, prefill-branch code).
  *
  *   q_nope [S, 128, 128], q_pe [S, 128, 64]
  *   kv_cache [T, 512], pe_cache [T, 64]   (start_pos + S <= T)

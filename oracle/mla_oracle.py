@@ -7,12 +7,12 @@ calls it and shares no code with it.
 What it computes, and where the pages define it
 ------------------------------------------------
 The oracle follows the *explicit* (non-absorbed) form that the model source
-uses for its prefill branch ("Key heads" page, code excerpt model.py 574-589,
-repeated on the "Rotated shared key" page):
+uses for its prefill branch ("Key heads" page, Explanation: the code of the
+prefill branch, repeated on the "Rotated shared key" page):
 
 1. ``wkv_b`` is one matrix whose per-head view is [128, 256, 512]; the first
    128 rows of each head are W_UK and the last 128 are W_UV ("Mix and project",
-   code model.py 590-606; "Key heads", Explanation: one matrix gives content
+   Explanation, decode-branch code; "Key heads", Explanation: one matrix gives content
    keys and values, split after the product).
 2. Each cached latent row is up-projected, ``kv = c . wkv_b^T``, viewed
    [rows, 128, 256] and split into per-head content keys k_nope (128) and
@@ -20,8 +20,8 @@ repeated on the "Rotated shared key" page):
 3. Per-head keys join the content part with the one rotary key shared by all
    heads: K_i = [K^C_i ; k^R] ("Key heads", equation K_i = [K^C_i; k^R]).
 4. Queries join q_nope and q_pe; scores are q . K scaled by
-   ``softmax_scale = qk_head_dim ** -0.5`` = 1/sqrt(192) ("Key heads", code
-   model.py 523-539).
+   ``softmax_scale = qk_head_dim ** -0.5`` = 1/sqrt(192) ("Key heads", Explanation,
+   the attention module's constructor).
 5. The index mask is -inf everywhere except at the listed positions, where it
    is 0 (``full(-inf).scatter_(..., topk, 0)``); prefill adds the causal mask
    ("Mix and project" and "Key heads" code).  Listing a position twice is the
@@ -278,7 +278,7 @@ def absorbed_scores(q_nope, q_pe, latent, rope, w_uk, scale=SOFTMAX_SCALE):
     """Decode-branch scores: W_UK folded into the query, scored on the latent.
 
     q_c[h, c] = sum_d q_nope[h, d] W_UK[h, d, c]; s[h, t] = (q_c[h] . c_t +
-    q_pe[h] . k^R_t) * scale ("Mix and project", code model.py 590-606).
+    q_pe[h] . k^R_t) * scale ("Mix and project", Explanation, decode-branch code).
     """
     q_c = np.einsum("hd,hdc->hc", to_f64(q_nope), to_f64(w_uk))
     return (q_c @ to_f64(latent).T + to_f64(q_pe) @ to_f64(rope).T) * scale
