@@ -903,9 +903,68 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
                 s_inv[mj] = inv;
                 marked[mj] = bad;
             }
-            // weights of the first staged group come from the values at hand
-            if (msub < kUvGroup) s_w[msub][mj] = (rr < R && msub < n_split) ? weight(m0, l0, mloc, inv) : 0.f;
+            // weights of the first staged group come from the values at hand; a
+            // head marked for exact recomputation takes nothing from its splits
+            if (msub < kUvGroup)
+                s_w[msub][mj] = (rr < R && msub < n_split && !bad) ? weight(m0, l0, mloc, inv) : 0.f;
         }
+        // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
+        const int j = lane & 31;
+        const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
+        auto uv_product = [&](int sl) {
+            f32x16 part = {};
+            const unsigned char* src = stage + sl * kUvRows * 1024;
+#pragma unroll
+            for (int ks = 0; ks < 32; ++ks) {
+                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(src + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+                part = mfma32(wa[ks], bv, part);
+            }
+            return part;
+        };
+        auto store_out = [&](const f32x16& acc) {
+            const int r = rb * kUvRows + j;
+            if (r < R) {
+                __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<bf16x4*>(dst + 8 * g) =
+                        to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+            }
+        };
+        if (n_split <= kUvGroup) {
+            // Every split is staged at once: multiply each split's bf16 partial
+            // by W_UV on its own and combine the products with the merge
+            // weights in float32 (the product is linear in O~).
+            __builtin_amdgcn_s_waitcnt(0);   // own partial rows landed
+            __syncthreads();                 // all rows, weights and flags visible
+            f32x16 acc = {};
+            for (int sl = 0; sl < n_split; ++sl) {
+                const f32x16 part = uv_product(sl);
+                const float w = s_w[sl][j];
+                if (w != 0.f)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[i] += w * part[i];
+            }
+            // heads whose attention pass was marked inexact: recompute exactly
+            int any = 0;
+            for (int row = 0; row < kUvRows; ++row) any |= marked[row];
+            if (any) {
+                __syncthreads();             // every staged row read
+                for (int row = 0; row < kUvRows; ++row) {
+                    if (!marked[row]) continue;
+                    exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
+                    for (int c = tid; c < kLatent; c += 256)
+                        *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
+                    __syncthreads();
+                }
+                const f32x16 part = uv_product(0);
+                if (marked[j]) acc = part;
+            }
+            store_out(acc);
+            __syncthreads();                 // staging reused by the next block
+            continue;
+        }
+
         float x[8][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -960,23 +1019,7 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
                 *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
             __syncthreads();
         }
-        // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
-        const int j = lane & 31;
-        const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(stage + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
-            acc = mfma32(wa[ks], bv, acc);
-        }
-        const int r = rb * kUvRows + j;
-        if (r < R) {
-            __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
-                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-        }
+        store_out(uv_product(0));
         __syncthreads();                     // staging reused by the next block
     }
 }
