@@ -112,15 +112,20 @@ __device__ __forceinline__ int wave_id() {
 constexpr int kWRow = 320;   // bytes per staged W_UK row (128 bf16 + pad)
 constexpr int kQcRow = 272;  // bytes per staged output row (128 bf16 + pad)
 
-__global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ q_nope,
-                                                     const __bf16* __restrict__ q_pe,
-                                                     const __bf16* __restrict__ w_uk,
-                                                     __bf16* __restrict__ q_out, int R,
-                                                     int r_groups) {
-    __shared__ __attribute__((aligned(16))) unsigned char wbuf[kNope * kWRow];
-    __shared__ __attribute__((aligned(16))) unsigned char obuf[32 * kQcRow];
-    const int h = blockIdx.x >> 2;
-    const int cq = blockIdx.x & 3;
+constexpr int kAbsorbLds = kNope * kWRow + 32 * kQcRow;   // LDS one absorb unit uses
+
+// One unit = (head h, quarter cq of the 512 latent columns), for query blocks
+// rb_first, rb_first + rb_step, ...; `lds` holds kAbsorbLds bytes.  Every
+// thread of the workgroup calls it.
+__device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
+                                            const __bf16* __restrict__ q_pe,
+                                            const __bf16* __restrict__ w_uk,
+                                            __bf16* __restrict__ q_out, int R, int unit,
+                                            int rb_first, int r_groups, unsigned char* lds) {
+    unsigned char* wbuf = lds;
+    unsigned char* obuf = lds + kNope * kWRow;
+    const int h = unit >> 2;
+    const int cq = unit & 3;
     const int tid = threadIdx.x;
     const int wave = wave_id();
     const int lane = tid & 63;
@@ -136,8 +141,8 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
     };
     const int blocks = (R + 31) / 32;
     bf16x8 b0[8], b1[8];
-    load_q(blockIdx.y, b0);
-    if (blockIdx.y + r_groups < blocks) load_q(blockIdx.y + r_groups, b1);
+    load_q(rb_first, b0);
+    if (rb_first + r_groups < blocks) load_q(rb_first + r_groups, b1);
 
     {
         // 128 rows d x 16 chunks of 8 columns; 8 chunks per thread
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
         __syncthreads();                  // obuf reused by the next block
     };
     // Two query blocks in flight: while one is multiplied, the next but one loads.
-    for (int rb = blockIdx.y; rb < blocks; rb += 2 * r_groups) {
+    for (int rb = rb_first; rb < blocks; rb += 2 * r_groups) {
         process(rb, b0);
         if (rb + 2 * r_groups < blocks) load_q(rb + 2 * r_groups, b0);
         if (rb + r_groups < blocks) {
@@ -208,6 +213,15 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
             if (rb + 3 * r_groups < blocks) load_q(rb + 3 * r_groups, b1);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ q_nope,
+                                                     const __bf16* __restrict__ q_pe,
+                                                     const __bf16* __restrict__ w_uk,
+                                                     __bf16* __restrict__ q_out, int R,
+                                                     int r_groups) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kAbsorbLds];
+    absorb_unit(q_nope, q_pe, w_uk, q_out, R, blockIdx.x, blockIdx.y, r_groups, lds);
 }
 
 // --------------------------------------------------------------------------
@@ -351,6 +365,11 @@ constexpr float kBeatenSum = 4294967296.f;   // 2^32
 // The reference of each head is the (scaled) maximum of its first tile with
 // a selected row; no rescaling happens afterwards.  `beaten` reports a tile
 // whose probabilities exceeded kBeatenSum against that reference.
+// kMode 0: the whole pass.  kMode 1: only the start of the prologue (index
+// list into LDS, gathers of tiles 0 and 1 issued, nothing waited for), so that
+// other work can run while they land.  kMode 2: the rest, after a kMode-1 call
+// whose loads have completed.
+template <int kMode>
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
                                           float& l_run, bool& beaten) {
     const int lane = c.lane;
@@ -363,20 +382,26 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // flight together.
     constexpr int kIdxPerThread = kMaxSlotsPerSplit / 256;
     int iv[kIdxPerThread];
+    if (kMode != 2) {
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
-        const int i = (int)threadIdx.x + 256 * u;
-        iv[u] = i < c.nslots ? c.idx_src[i] : -1;
+        for (int u = 0; u < kIdxPerThread; ++u) {
+            const int i = (int)threadIdx.x + 256 * u;
+            iv[u] = i < c.nslots ? c.idx_src[i] : -1;
+        }
     }
     bf16x8 qf[36];
+    if (kMode != 1) {
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 16 * ks);
-#pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
-        const int i = (int)threadIdx.x + 256 * u;
-        if (i < ntiles * kRows) c.sidx[i] = iv[u];
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 16 * ks);
     }
-    barrier_lds();
+    if (kMode != 2) {
+#pragma unroll
+        for (int u = 0; u < kIdxPerThread; ++u) {
+            const int i = (int)threadIdx.x + 256 * u;
+            if (i < ntiles * kRows) c.sidx[i] = iv[u];
+        }
+        barrier_lds();
+    }
 
     // Per-lane LDS offsets, relative to a tile buffer.  Buffer offsets are
     // multiples of 512 bytes, so XOR-ing a compile-time constant into bits 5..7
@@ -601,8 +626,11 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
     l_run = 0.f;
-    gather_tile(0);
-    gather_tile(1);
+    if (kMode != 2) {
+        gather_tile(0);
+        gather_tile(1);
+    }
+    if (kMode == 1) return;
     gather_tile(2);
     __builtin_amdgcn_s_waitcnt(0);       // query fragments and the first three tiles
     barrier_only();
@@ -670,20 +698,15 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
-    __shared__ __attribute__((aligned(1024))) unsigned char tiles[kBufs * kBufBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char pbuf[kHeads * kPRow];
-    __shared__ int sidx[kMaxSlotsPerSplit];
-
-    // Workgroup -> (query row, split).  Consecutive workgroups land on the 8
-    // XCDs in turn; the splits of one query row share an XCD, so its absorbed
-    // query is read from HBM once.  Latest query rows (most work) go first.
-    const int id = blockIdx.x;
+// Workgroup slot -> (query row, split).  Consecutive slots land on the 8 XCDs
+// in turn; the splits of one query row share an XCD, so its absorbed query is
+// read from HBM once.  Latest query rows (most work) go first.  Returns false
+// for a slot past the last row.
+__device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& a, int id, unsigned char* tiles,
+                                           unsigned char* pbuf, int* sidx) {
     const int split = (id >> 3) % a.n_split;
     const int rr = ((id >> 3) / a.n_split) * 8 + (id & 7);
-    if (rr >= a.R) return;
-
-    SplitCtx c;
+    if (rr >= a.R) return false;
     c.a = &a;
     c.tiles = tiles;
     c.pbuf = pbuf;
@@ -698,19 +721,30 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
     c.limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + c.r;
     c.T = a.T;
     c.kv_desc = make_desc_x4(reinterpret_cast<const __bf16*>(a.kv) + (size_t)c.r * a.cache_rows_per_query * kLatent,
-                          (unsigned)c.T * (kLatent * 2));
+                             (unsigned)c.T * (kLatent * 2));
     c.pe_desc = make_desc(reinterpret_cast<const __bf16*>(a.pe) + (size_t)c.r * a.cache_rows_per_query * kRope,
                           (unsigned)c.T * (kRope * 2));
     c.qrow = reinterpret_cast<const __bf16*>(a.q) +
              ((size_t)c.r * kHeads + 32 * c.wave + (c.lane & 31)) * kQRow + 8 * (c.lane >> 5);
-
     c.idx_src = a.idx + (size_t)c.r * a.k + slot_begin;
     c.nslots = nslots;
+    return true;
+}
 
+// LDS of the attention pass: tile buffers, one tile's probabilities, the split's index list.
+constexpr int kAttnTilesLds = kBufs * kBufBytes;
+constexpr int kAttnLds = kAttnTilesLds + kHeads * kPRow + kMaxSlotsPerSplit * 4;
+
+__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttnLds];
+    SplitCtx c;
+    if (!attn_setup(c, a, blockIdx.x, lds, lds + kAttnTilesLds,
+                    reinterpret_cast<int*>(lds + kAttnTilesLds + kHeads * kPRow)))
+        return;
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
     bool beaten = false;
-    attn_pass(c, m_ref, acc, l_run, beaten);
+    attn_pass<0>(c, m_ref, acc, l_run, beaten);
     attn_finish(c, acc, m_ref, l_run, beaten);
 }
 
@@ -800,19 +834,34 @@ __device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* r
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
-                                                  __bf16* __restrict__ out, int r_groups) {
-    __shared__ __attribute__((aligned(1024))) unsigned char stage[kUvStage];
-    __shared__ float s_mmax[kUvRows], s_inv[kUvRows];
-    __shared__ float s_w[kUvGroup][kUvRows];
-    __shared__ int marked[kUvRows];
-    __shared__ float xo[kLatent];
-    __shared__ float xred[4];
-    __shared__ float xp[256];
-    __shared__ int xpos[256];
+// LDS of one merge + W_UV block: staged partials, then small per-row arrays.
+constexpr int kUvSmall = (2 * kUvRows + kUvGroup * kUvRows + kUvRows + kLatent + 4 + 256 + 256) * 4;
+constexpr int kUvLds = kUvStage + kUvSmall;
+
+// Wave w's slice of W_UV[h] (rows d = 32w .. 32w+31) as MFMA A fragments.
+__device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h, bf16x8 (&wa)[32]) {
+    const int lane = threadIdx.x & 63;
+    const int d = 32 * wave_id() + (lane & 31);
+    const __bf16* wrow = w_uv + ((size_t)h * kValue + d) * kLatent + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
+}
+
+// Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31; `lds` holds kUvLds
+// bytes (1 KiB aligned).  Every thread of the workgroup calls it.
+__device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__ out, int h, int rb,
+                                         const bf16x8 (&wa)[32], unsigned char* lds) {
+    unsigned char* stage = lds;
+    float* s_mmax = reinterpret_cast<float*>(lds + kUvStage);
+    float* s_inv = s_mmax + kUvRows;
+    float (*s_w)[kUvRows] = reinterpret_cast<float (*)[kUvRows]>(s_inv + kUvRows);
+    int* marked = reinterpret_cast<int*>(s_inv + kUvRows + kUvGroup * kUvRows);
+    float* xo = reinterpret_cast<float*>(marked + kUvRows);
+    float* xred = xo + kLatent;
+    float* xp = xred + 4;
+    int* xpos = reinterpret_cast<int*>(xp + 256);
     const int R = a.R;
     const int n_split = a.n_split;
-    const int h = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = wave_id();
     const int lane = tid & 63;
@@ -852,19 +901,13 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
         return l > 0.f ? w : 0.f;
     };
 
-    bf16x8 wa[32];
-    {
-        const __bf16* wrow = w_uv + ((size_t)h * kValue + d) * kLatent + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
-    }
 
     // merge lanes: thread -> staged row mj, chunks mp[i] = 8i + (tid % 8), with
     // the 8-chunk groups of odd rows rotated to spread LDS banks
     const int mj = tid >> 3;
     const int msub = tid & 7;
 
-    for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups) {
+    {
         stage_group(rb, 0);
         // per-row maximum, inverse weight sum and inexact flag over all splits;
         // lanes mj*8 .. mj*8+7 share row mj, lane msub takes splits msub + 8i
@@ -962,7 +1005,7 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
             }
             store_out(acc);
             __syncthreads();                 // staging reused by the next block
-            continue;
+            return;
         }
 
         float x[8][8];
@@ -1022,6 +1065,15 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
         store_out(uv_product(0));
         __syncthreads();                     // staging reused by the next block
     }
+}
+
+__global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
+                                                  __bf16* __restrict__ out, int r_groups) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvLds];
+    const int h = blockIdx.x;
+    bf16x8 wa[32];
+    uv_load_w(w_uv, h, wa);
+    for (int rb = blockIdx.y; rb * kUvRows < a.R; rb += r_groups) uv_block(a, out, h, rb, wa, lds);
 }
 
 }  // namespace
