@@ -907,6 +907,136 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     const int mj = tid >> 3;
     const int msub = tid & 7;
 
+    // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
+    const int j = lane & 31;
+    const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
+    auto uv_product = [&](int sl) {
+        f32x16 part = {};
+        const unsigned char* src = stage + sl * kUvRows * 1024;
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(src + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+            part = mfma32(wa[ks], bv, part);
+        }
+        return part;
+    };
+    auto store_out = [&](const f32x16& acc) {
+        const int r = rb * kUvRows + j;
+        if (r < R) {
+            __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
+                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+    };
+    // heads whose attention pass was marked inexact: recompute exactly into
+    // staged slot 0 and give those columns its product instead
+    auto exact_heads = [&](f32x16& acc) {
+        int any = 0;
+        for (int row = 0; row < kUvRows; ++row) any |= marked[row];
+        if (!any) return;
+        __syncthreads();                     // every staged row read
+        for (int row = 0; row < kUvRows; ++row) {
+            if (!marked[row]) continue;
+            exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
+            for (int c = tid; c < kLatent; c += 256)
+                *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
+            __syncthreads();
+        }
+        const f32x16 part = uv_product(0);
+        if (marked[j]) acc = part;
+    };
+
+    if (n_split <= kUvGroup) {
+        // Every split fits in LDS at once.  Each wave loads rows 8w .. 8w+7
+        // of every split, split by split, and each split is multiplied by
+        // W_UV as soon as it has landed while the later ones are in flight;
+        // the products are combined with the merge weights in float32 (the
+        // product is linear in O~).  The per-split maxima and sums are loaded
+        // first, so that they are the oldest loads in flight.
+        const int rr_m = rb * kUvRows + mj;
+        const bool have = rr_m < R && msub < n_split;
+        float m0 = -INFINITY, l0 = 0.f;
+        if (have) {
+            const size_t o = ((size_t)msub * R + rr_m) * kHeads + h;
+            l0 = a.l_part[o];
+            m0 = a.m_part[o];
+        }
+        {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const unsigned row_bytes = kHeads * kLatent * 2;
+            for (int sp = 0; sp < n_split; ++sp) {
+                const __bf16* src0 = o_ws + (((size_t)sp * R + rb * kUvRows) * kHeads + h) * kLatent;
+                const u32x4 desc = make_desc_x4(src0, (unsigned)min(R - rb * kUvRows, kUvRows) * row_bytes);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int j0 = 8 * wave + 4 * g;
+                    unsigned v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int jj = j0 + u;
+                        const bool ok = rb * kUvRows + jj < R;
+                        v[u] = x4_off(ok, (unsigned)jj * row_bytes +
+                                              (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(jj))) << 4), u);
+                    }
+                    load_lds16_x4(desc, stage_addr + (sp * kUvRows + j0) * 1024, v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+        f32x16 part[kUvGroup];
+#pragma unroll
+        for (int sl = 0; sl < kUvGroup; ++sl) {
+            if (sl >= n_split) break;
+            // own loads of split sl done: the later splits' 8 each may remain
+            switch (n_split - 1 - sl) {
+                case 0: MLA_WAIT_VMCNT(0); break;
+                case 1: MLA_WAIT_VMCNT(8); break;
+                case 2: MLA_WAIT_VMCNT(16); break;
+                default: MLA_WAIT_VMCNT(24); break;
+            }
+            barrier_only();                  // every wave's rows of split sl landed
+            part[sl] = uv_product(sl);
+        }
+        // merge weights: lane msub of row mj holds split msub's (m, l)
+        float mloc = -INFINITY, wloc = 0.f;
+        int bad = 0;
+        if (have) {
+            bad = l0 < 0.f;
+            if (l0 > 0.f) {
+                mloc = m0;
+                wloc = l0;
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            const float m2 = __shfl_xor(mloc, o);
+            const float w2 = __shfl_xor(wloc, o);
+            const float mx = fmaxf(mloc, m2);
+            wloc = (wloc > 0.f ? wloc * exp2f(mloc - mx) : 0.f) + (w2 > 0.f ? w2 * exp2f(m2 - mx) : 0.f);
+            mloc = mx;
+            bad |= __shfl_xor(bad, o);
+        }
+        const float inv = wloc > 0.f ? 1.f / wloc : 0.f;
+        if (msub == 0) marked[mj] = bad;
+        if (msub < kUvGroup) s_w[msub][mj] = (have && !bad) ? weight(m0, l0, mloc, inv) : 0.f;
+        __syncthreads();
+        f32x16 acc = {};
+#pragma unroll
+        for (int sl = 0; sl < kUvGroup; ++sl) {
+            if (sl >= n_split) break;
+            const float w = s_w[sl][j];
+            if (w != 0.f)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] += w * part[sl][i];
+        }
+        exact_heads(acc);
+        store_out(acc);
+        __syncthreads();                     // staging reused by the next block
+        return;
+    }
+
     {
         stage_group(rb, 0);
         // per-row maximum, inverse weight sum and inexact flag over all splits;
@@ -951,63 +1081,6 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
             if (msub < kUvGroup)
                 s_w[msub][mj] = (rr < R && msub < n_split && !bad) ? weight(m0, l0, mloc, inv) : 0.f;
         }
-        // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
-        const int j = lane & 31;
-        const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
-        auto uv_product = [&](int sl) {
-            f32x16 part = {};
-            const unsigned char* src = stage + sl * kUvRows * 1024;
-#pragma unroll
-            for (int ks = 0; ks < 32; ++ks) {
-                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(src + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
-                part = mfma32(wa[ks], bv, part);
-            }
-            return part;
-        };
-        auto store_out = [&](const f32x16& acc) {
-            const int r = rb * kUvRows + j;
-            if (r < R) {
-                __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<bf16x4*>(dst + 8 * g) =
-                        to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-            }
-        };
-        if (n_split <= kUvGroup) {
-            // Every split is staged at once: multiply each split's bf16 partial
-            // by W_UV on its own and combine the products with the merge
-            // weights in float32 (the product is linear in O~).
-            __builtin_amdgcn_s_waitcnt(0);   // own partial rows landed
-            __syncthreads();                 // all rows, weights and flags visible
-            f32x16 acc = {};
-            for (int sl = 0; sl < n_split; ++sl) {
-                const f32x16 part = uv_product(sl);
-                const float w = s_w[sl][j];
-                if (w != 0.f)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[i] += w * part[i];
-            }
-            // heads whose attention pass was marked inexact: recompute exactly
-            int any = 0;
-            for (int row = 0; row < kUvRows; ++row) any |= marked[row];
-            if (any) {
-                __syncthreads();             // every staged row read
-                for (int row = 0; row < kUvRows; ++row) {
-                    if (!marked[row]) continue;
-                    exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
-                    for (int c = tid; c < kLatent; c += 256)
-                        *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
-                    __syncthreads();
-                }
-                const f32x16 part = uv_product(0);
-                if (marked[j]) acc = part;
-            }
-            store_out(acc);
-            __syncthreads();                 // staging reused by the next block
-            return;
-        }
-
         float x[8][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
