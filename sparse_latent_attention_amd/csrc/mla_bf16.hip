@@ -95,6 +95,16 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// Layout of the absorbed queries in the workspace, chosen for the attention
+// waves' score operands: element c (0..575: 512 latent, then 64 rotary) of
+// head h of query row r sits at
+//   ((r*4 + h/32)*36 + c/16)*512 + (h%32)*16 + c%16,
+// so the 16-byte operand loads of one wave and k-step read one contiguous
+// 1 KiB run, and the absorption writes 32-byte runs.
+__device__ __forceinline__ size_t q_off(int r, int h, int c) {
+    return (((size_t)r * 4 + (h >> 5)) * 36 + (c >> 4)) * 512 + (size_t)((h & 31) * 16) + (c & 15);
+}
+
 // --------------------------------------------------------------------------
 // Step 1: q_c[r, h, :] = q_nope[r, h, :] . W_UK[h]  (and append q_pe)
 //
@@ -190,7 +200,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             const int e = tid + 256 * i;
             const int rr = rb * 32 + (e >> 4);
             if (rr < R)
-                *reinterpret_cast<u32x4*>(q_out + ((size_t)rr * kHeads + h) * kQRow + cq * 128 + 8 * (e & 15)) =
+                *reinterpret_cast<u32x4*>(q_out + q_off(rr, h, cq * 128 + 8 * (e & 15))) =
                     *reinterpret_cast<const u32x4*>(obuf + (e >> 4) * kQcRow + 16 * (e & 15));
         }
         if (cq == 0) {
@@ -198,7 +208,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             const int rr = rb * 32 + (tid >> 3);
             const int ch = tid & 7;
             if (rr < R) {
-                *reinterpret_cast<bf16x8*>(q_out + ((size_t)rr * kHeads + h) * kQRow + kLatent + 8 * ch) =
+                *reinterpret_cast<bf16x8*>(q_out + q_off(rr, h, kLatent + 8 * ch)) =
                     *reinterpret_cast<const bf16x8*>(q_pe + ((size_t)rr * kHeads + h) * kRope + 8 * ch);
             }
         }
@@ -347,7 +357,7 @@ struct SplitCtx {
     int* sidx;                   // the split's index list in LDS (-1 past its end)
     const int32_t* idx_src;      // the split's index list in global memory
     int nslots;                  // its length
-    const __bf16* qrow;          // this lane's absorbed-query row, offset to its k half
+    const __bf16* qrow;          // this lane's score operands: k-step ks at qrow + 512*ks
     u32x4 kv_desc, pe_desc;
     int r, split, ntiles, limit, T, wave, lane;
 };
@@ -392,7 +402,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     bf16x8 qf[36];
     if (kMode != 1) {
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 16 * ks);
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 512 * ks);
     }
     if (kMode != 2) {
 #pragma unroll
@@ -724,8 +734,7 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& a, int i
                              (unsigned)c.T * (kLatent * 2));
     c.pe_desc = make_desc(reinterpret_cast<const __bf16*>(a.pe) + (size_t)c.r * a.cache_rows_per_query * kRope,
                           (unsigned)c.T * (kRope * 2));
-    c.qrow = reinterpret_cast<const __bf16*>(a.q) +
-             ((size_t)c.r * kHeads + 32 * c.wave + (c.lane & 31)) * kQRow + 8 * (c.lane >> 5);
+    c.qrow = reinterpret_cast<const __bf16*>(a.q) + q_off(c.r, 32 * c.wave + (c.lane & 31), 8 * (c.lane >> 5));
     c.idx_src = a.idx + (size_t)c.r * a.k + slot_begin;
     c.nslots = nslots;
     return true;
@@ -780,15 +789,16 @@ __device__ __forceinline__ int uv_pos(int j, int col) {
 __device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* red, float* p_s,
                           int* pos_s) {
     const int tid = threadIdx.x;
-    const __bf16* q = reinterpret_cast<const __bf16*>(a.q) + ((size_t)rr * kHeads + h) * kQRow;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q);
     const __bf16* kv = reinterpret_cast<const __bf16*>(a.kv) + (size_t)rr * a.cache_rows_per_query * kLatent;
     const __bf16* pe = reinterpret_cast<const __bf16*>(a.pe) + (size_t)rr * a.cache_rows_per_query * kRope;
     const int32_t* idx = a.idx + (size_t)rr * a.k;
     const int limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + rr;
     auto score = [&](int t) {
         float d = 0.f;
-        for (int c = 0; c < kLatent; ++c) d += (float)q[c] * (float)kv[(size_t)t * kLatent + c];
-        for (int c = 0; c < kRope; ++c) d += (float)q[kLatent + c] * (float)pe[(size_t)t * kRope + c];
+        for (int c = 0; c < kLatent; ++c) d += (float)qb[q_off(rr, h, c)] * (float)kv[(size_t)t * kLatent + c];
+        for (int c = 0; c < kRope; ++c)
+            d += (float)qb[q_off(rr, h, kLatent + c)] * (float)pe[(size_t)t * kRope + c];
         return d * a.scale_log2;
     };
     auto block_max = [&](float v) {
