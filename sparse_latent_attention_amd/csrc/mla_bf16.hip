@@ -231,7 +231,14 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
                                                      __bf16* __restrict__ q_out, int R,
                                                      int r_groups) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kAbsorbLds];
-    absorb_unit(q_nope, q_pe, w_uk, q_out, R, blockIdx.x, blockIdx.y, r_groups, lds);
+    // Workgroups are dealt to the eight XCDs in turn (id % 8).  XCD x takes
+    // heads 16x .. 16x+15 with all four column quarters, so a head's queries
+    // come from memory once per launch (the other quarters hit that XCD's L2)
+    // and the 32-byte output pieces of neighbouring heads, which share cache
+    // lines, are merged in one L2 before they are written back.
+    const int b = blockIdx.x, j = b >> 3;
+    absorb_unit(q_nope, q_pe, w_uk, q_out, R, (16 * (b & 7) + (j >> 2)) * 4 + (j & 3), blockIdx.y,
+                r_groups, lds);
 }
 
 // --------------------------------------------------------------------------
