@@ -451,29 +451,39 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     const int jp = lane >> 3;                          // rotary row of this lane's gather
     const unsigned pe_lane = (unsigned)(((lane & 7) ^ jp) << 4);
 
-    // Gathers.  Lane l reads the index of row 8*wave + l/8 of the tile: it
-    // addresses that row's rotary part, and lanes 8q .. 8q+7 hold the index of
-    // latent row q, which is read back as a wave-uniform value.  A tile index
+    // Gathers.  Wave w fetches rows 8w .. 8w+7 of a tile: their latent parts
+    // (eight 1 KiB loads) and their rotary parts (one load, lane l takes
+    // 16 bytes of row 8w + l/8, whose index it reads itself).  A tile index
     // >= ntiles issues the same nine loads with out-of-range offsets (they
     // touch no memory), so every gather adds exactly nine to vmcnt.
     auto gather_index = [&](int t) -> int {
         return c.sidx[min(t, ntiles - 1) * kRows + 8 * c.wave + jp];
     };
-    // latent rows 8*wave + 4*g .. +3 of tile t (one M0 value for the four)
-    auto gather_rows4 = [&](int t, int pidx, int g) {
+    // Latent rows 8*wave + 4*g .. +3 of tile t, with one M0 value for the
+    // four.  Their indices are adjacent in the LDS list: one broadcast read
+    // gives all four to every lane (rows_index), and each row's offset is
+    // plain vector arithmetic (row_offset), which the tile loop spreads over
+    // several k-steps of the score chain.
+    auto rows_index = [&](int t, int g) -> u32x4 {
+        return *(const __attribute__((address_space(3))) u32x4*)(
+            (const __attribute__((address_space(3))) int*)c.sidx + min(t, ntiles - 1) * kRows + 8 * c.wave + 4 * g);
+    };
+    auto row_offset = [&](int t, const u32x4& pv, int g, int u) -> unsigned {
         const unsigned lim_t = t < ntiles ? lim : 0u;
         int ln = lane;
         asm volatile("" : "+v"(ln));   // keep the per-row lane offsets out of the loop
-        unsigned v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = 4 * g + u;
-            const unsigned p = (unsigned)__builtin_amdgcn_readlane(pidx, 8 * q);
-            const int row = 8 * c.wave + q;
-            v[u] = x4_off(p < lim_t, (p << 10) + ((unsigned)(ln ^ lat_swz(row)) << 4), u);
-        }
+        return x4_off(pv[u] < lim_t, (pv[u] << 10) + ((unsigned)(ln ^ lat_swz(8 * c.wave + 4 * g + u)) << 4), u);
+    };
+    auto issue_rows4 = [&](int t, int g, const unsigned (&v)[4]) {
         load_lds16_x4(c.kv_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + (8 * c.wave + 4 * g) * 1024,
                       v[0], v[1], v[2], v[3]);
+    };
+    auto gather_rows4 = [&](int t, int g) {
+        const u32x4 pv = rows_index(t, g);
+        unsigned v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = row_offset(t, pv, g, u);
+        issue_rows4(t, g, v);
     };
     auto gather_pe = [&](int t, int pidx) {
         const unsigned lim_t = t < ntiles ? lim : 0u;
@@ -482,10 +492,9 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
                    off);
     };
     auto gather_tile = [&](int t) {
-        const int pidx = gather_index(t);
-        gather_rows4(t, pidx, 0);
-        gather_rows4(t, pidx, 1);
-        gather_pe(t, pidx);
+        gather_rows4(t, 0);
+        gather_rows4(t, 1);
+        gather_pe(t, gather_index(t));
     };
 
     // Score operand (A) for k-step ks of the tile in buffer offset bo.
@@ -606,6 +615,8 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         barrier_only();                  // all of t+1 landed; every wave is done with t-1 and P
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
+        const u32x4 pv[2] = {rows_index(t + 3, 0), rows_index(t + 3, 1)};
+        unsigned goff[2][4];
         bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
         bf16x8 pb[2];
         float psum = 0.f;
@@ -617,11 +628,20 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
             else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
             else mfma32_v_last(snext, sacc, av, qf[ks]);
-            if (ks < 16) prob(scur, ks, sc, neg_m, pb, psum);
-            if (ks == 16) close_sum(psum);
-            if (ks == 17) store_p(pb);
-            if (ks == 18) gather_rows4(t + 3, pidx, 0);
-            if (ks == 26) gather_rows4(t + 3, pidx, 1);
+            // one exponential every other k-step, so that each fits in the
+            // shadow of the MFMA in flight
+            if (ks < 32 && !(ks & 1)) prob(scur, ks >> 1, sc, neg_m, pb, psum);
+            if (ks == 32) close_sum(psum);
+            if (ks == 33) store_p(pb);
+            if ((ks & 1) && ks < 16) {
+                // one gather offset per odd k-step (the even ones carry an
+                // exponential); the empty asm keeps it from being bunched up
+                const int gg = ks >> 3, u = (ks >> 1) & 3;
+                goff[gg][u] = row_offset(t + 3, pv[gg], gg, u);
+                asm volatile("" : "+v"(goff[gg][u]));
+            }
+            if (ks == 18) issue_rows4(t + 3, 0, goff[0]);
+            if (ks == 26) issue_rows4(t + 3, 1, goff[1]);
         }
         barrier_lds();                   // every head's probabilities of tile t in LDS
         mix(t, [&] { gather_pe(t + 3, pidx); });
