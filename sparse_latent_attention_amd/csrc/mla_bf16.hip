@@ -382,11 +382,6 @@ constexpr float kBeatenSum = 4294967296.f;   // 2^32
 // The reference of each head is the (scaled) maximum of its first tile with
 // a selected row; no rescaling happens afterwards.  `beaten` reports a tile
 // whose probabilities exceeded kBeatenSum against that reference.
-// kMode 0: the whole pass.  kMode 1: only the start of the prologue (index
-// list into LDS, gathers of tiles 0 and 1 issued, nothing waited for), so that
-// other work can run while they land.  kMode 2: the rest, after a kMode-1 call
-// whose loads have completed.
-template <int kMode>
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
                                           float& l_run, bool& beaten) {
     const int lane = c.lane;
@@ -399,26 +394,20 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // flight together.
     constexpr int kIdxPerThread = kMaxSlotsPerSplit / 256;
     int iv[kIdxPerThread];
-    if (kMode != 2) {
 #pragma unroll
-        for (int u = 0; u < kIdxPerThread; ++u) {
-            const int i = (int)threadIdx.x + 256 * u;
-            iv[u] = i < c.nslots ? c.idx_src[i] : -1;
-        }
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        iv[u] = i < c.nslots ? c.idx_src[i] : -1;
     }
     bf16x8 qf[36];
-    if (kMode != 1) {
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 512 * ks);
-    }
-    if (kMode != 2) {
+    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 512 * ks);
 #pragma unroll
-        for (int u = 0; u < kIdxPerThread; ++u) {
-            const int i = (int)threadIdx.x + 256 * u;
-            if (i < ntiles * kRows) c.sidx[i] = iv[u];
-        }
-        barrier_lds();
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        if (i < ntiles * kRows) c.sidx[i] = iv[u];
     }
+    barrier_lds();
 
     // Per-lane LDS offsets, relative to a tile buffer.  Buffer offsets are
     // multiples of 512 bytes, so XOR-ing a compile-time constant into bits 5..7
@@ -663,13 +652,10 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
     l_run = 0.f;
-    if (kMode != 2) {
-        gather_tile(0);
-        gather_tile(1);
-    }
-    if (kMode == 1) return;
+    gather_tile(0);
+    gather_tile(1);
     gather_tile(2);
-    __builtin_amdgcn_s_waitcnt(0);       // query fragments and the first three tiles
+    MLA_WAIT_VMCNT(18);                  // query fragments and tile 0 (tiles 1, 2 may still be in flight)
     barrier_only();
     f32x16 sA, sB;
     scores(0, sA);
@@ -780,7 +766,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
     bool beaten = false;
-    attn_pass<0>(c, m_ref, acc, l_run, beaten);
+    attn_pass(c, m_ref, acc, l_run, beaten);
     attn_finish(c, acc, m_ref, l_run, beaten);
 }
 
