@@ -369,6 +369,14 @@ struct SplitCtx {
     int r, split, ntiles, limit, T, wave, lane;
 };
 
+// Score operands read ahead of their MFMA: LDS reads only reach full
+// bandwidth with many in flight per wave, and every wave streams a whole tile
+// through the score chain.
+#ifndef MLA_SC_DEPTH
+#define MLA_SC_DEPTH 6
+#endif
+constexpr int kScDepth = MLA_SC_DEPTH;
+
 // A head whose per-tile probability sum exceeds this (relative to its
 // reference) is recomputed exactly by the merge; below it, no probability or
 // partial sum comes near the float/bf16 range.
@@ -497,11 +505,13 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     auto scores = [&](int t, f32x16& out) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
         f32x16 sacc;
-        bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
+        bf16x8 pre[kScDepth];
+#pragma unroll
+        for (int d = 0; d < kScDepth; ++d) pre[d] = sc_read(bo, d);
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8 av = pre[ks & 3];
-            if (ks + 4 < 36) pre[ks & 3] = sc_read(bo, ks + 4);
+            const bf16x8 av = pre[ks % kScDepth];
+            if (ks + kScDepth < 36) pre[ks % kScDepth] = sc_read(bo, ks + kScDepth);
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
             else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
             else mfma32_v_last(out, sacc, av, qf[ks]);
@@ -564,7 +574,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // Mix of the wave's quarter of the latent columns for all 128 heads:
     // O~^T[c][h] += V^T[c][j] P^T[j][h], c = 128*wave + 32*cbi + (0..31),
     // h = 32*hb + (0..31); acc[4*cbi + hb].
-    auto mix = [&](int t, auto&& side) {
+    auto mix = [&](int t, auto&& before, auto&& after) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
         const int y = c.wave * 256;
         auto v_read = [&](int idx) -> bf16x8 {      // idx = 4*kc + cbi
@@ -588,32 +598,52 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) pk[1][hb] = p_read(hb, 1);
             const int kc = idx >> 2, cbi = idx & 3;
+            before(idx);
+            // keep the last MFMAs below whatever before() issued
+            if (idx == 7) asm volatile("" : "+v"(va[1]));
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)
                 acc[4 * cbi + hb] = mfma32(va[idx & 1], pk[kc][hb], acc[4 * cbi + hb]);
-            if (idx == 3) side();
+            after(idx);
         }
     };
 
-    // Iteration t with a next tile: scores of t+1 into snext, softmax of t
-    // from scur, gather of t+3, then the mix of t.
+    // Score operands of the next chain, read ahead (kept across iterations).
+    bf16x8 pre[kScDepth];
+    auto preload = [&](int t) {
+        const int bo = (t & (kBufs - 1)) * kBufBytes;
+#pragma unroll
+        for (int d = 0; d < kScDepth; ++d) pre[d] = sc_read(bo, d);
+    };
+    // Hand-over to the next iteration, placed before the last MFMAs of a mix
+    // so that they cover the latency of the next chain's first reads: own
+    // gathers of tile tn landed (the tile after it may stay in flight), then
+    // a barrier after which tile tn is complete and every wave is done
+    // reading the mixed tile and P.
+    auto hand_over = [&](int tn) {
+        MLA_WAIT_VMCNT(9);
+        barrier_lds();
+        preload(tn);
+        asm volatile("" ::: "memory");   // issue the reads here, not at their first use
+    };
+
+    // Iteration t with a next tile (tile t+1 complete and its first operands
+    // read ahead): scores of t+1 into snext, softmax of t from scur, gather
+    // of t+3, then the mix of t, with the hand-over to iteration t+1.
     auto body = [&](int t, f32x16& scur, f32x16& snext) {
         const float sc = prepare(t, scur);
         const float neg_m = have_ref ? -m_ref : 0.f;
-        MLA_WAIT_VMCNT(9);               // own gathers of t+1 done (t+2 may stay in flight)
-        barrier_only();                  // all of t+1 landed; every wave is done with t-1 and P
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
         const u32x4 pv[2] = {rows_index(t + 3, 0), rows_index(t + 3, 1)};
         unsigned goff[2][4];
-        bf16x8 pre[4] = {sc_read(bo, 0), sc_read(bo, 1), sc_read(bo, 2), sc_read(bo, 3)};
         bf16x8 pb[2];
         float psum = 0.f;
         f32x16 sacc;
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8 av = pre[ks & 3];
-            if (ks + 4 < 36) pre[ks & 3] = sc_read(bo, ks + 4);
+            const bf16x8 av = pre[ks % kScDepth];
+            if (ks + kScDepth < 36) pre[ks % kScDepth] = sc_read(bo, ks + kScDepth);
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
             else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
             else mfma32_v_last(snext, sacc, av, qf[ks]);
@@ -633,7 +663,8 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             if (ks == 26) issue_rows4(t + 3, 1, goff[1]);
         }
         barrier_lds();                   // every head's probabilities of tile t in LDS
-        mix(t, [&] { gather_pe(t + 3, pidx); });
+        mix(t, [&](int idx) { if (idx == 7) hand_over(t + 2); },
+               [&](int idx) { if (idx == 3) gather_pe(t + 3, pidx); });
     };
     // Last tile: softmax and mix only.
     auto last = [&](int t, f32x16& scur) {
@@ -646,19 +677,26 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         close_sum(psum);
         store_p(pb);
         barrier_lds();
-        mix(t, [] {});
+        mix(t, [](int) {}, [](int) {});
     };
 
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
     l_run = 0.f;
+    // The first score chain needs the query fragments and tile 0 only.  The
+    // wait for them is a full one: the compiler does not see the gathers
+    // (inline assembly), so after a partial wait it would still take the
+    // later query loads for pending and wait again inside the chain, on
+    // counts that include the gathers of tiles 1 and 2.  Those two go out
+    // once the wait is over.
     gather_tile(0);
+    __builtin_amdgcn_s_waitcnt(0);
     gather_tile(1);
     gather_tile(2);
-    MLA_WAIT_VMCNT(18);                  // query fragments and tile 0 (tiles 1, 2 may still be in flight)
     barrier_only();
     f32x16 sA, sB;
     scores(0, sA);
+    if (ntiles > 1) hand_over(1);
     int t = 0;
     for (; t + 1 < ntiles; ++t) {
         body(t, sA, sB);
