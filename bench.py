@@ -42,8 +42,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic_b64_t32k_k2048.
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--sets", type=int, default=8, help="independently seeded query sets to rotate")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0,
