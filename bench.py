@@ -43,7 +43,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=1000,
+                   help="untimed steps first: clocks and address translation need tens of ms of load to settle")
     p.add_argument("--sets", type=int, default=8, help="independently seeded query sets to rotate")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0,
