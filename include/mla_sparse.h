@@ -61,7 +61,7 @@ extern "C" {
 #define MLA_D_ROPE 64
 #define MLA_D_NOPE 128
 #define MLA_D_V 128
-#define MLA_MAX_T 2097151   /* largest cache length T (positions per sequence) */
+#define MLA_MAX_T 2097148   /* largest cache length T (positions per sequence) */
 
 typedef enum {
     MLA_OK = 0,

@@ -461,12 +461,23 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // gives all four to every lane (rows_index), and each row's offset is
     // plain vector arithmetic (row_offset), which the tile loop spreads over
     // several k-steps of the score chain.
+    // The read's address goes through an opaque per-lane zero: the indices
+    // are the same in every lane, and the compiler would otherwise move them
+    // to scalar registers and test them there, a chain of lane-to-scalar
+    // moves, scalar compares and vector selects that stalls the MFMA chain;
+    // in vector registers each offset is three independent instructions.
     auto rows_index = [&](int t, int g) -> u32x4 {
+        int lz = 0;
+        asm volatile("" : "+v"(lz));
         return *(const __attribute__((address_space(3))) u32x4*)(
-            (const __attribute__((address_space(3))) int*)c.sidx + min(t, ntiles - 1) * kRows + 8 * c.wave + 4 * g);
+            (const __attribute__((address_space(3))) int*)c.sidx + min(t, ntiles - 1) * kRows + 8 * c.wave + 4 * g + lz);
     };
     auto row_offset = [&](int t, const u32x4& pv, int g, int u) -> unsigned {
-        const unsigned lim_t = t < ntiles ? lim : 0u;
+        // one vector compare against a scalar limit (0 past the last tile);
+        // the compiler would otherwise test the tile in a scalar mask and
+        // combine the two, moving the condition between the units
+        unsigned lim_t = t < ntiles ? lim : 0u;
+        asm volatile("" : "+s"(lim_t));
         int ln = lane;
         asm volatile("" : "+v"(ln));   // keep the per-row lane offsets out of the loop
         return x4_off(pv[u] < lim_t, (pv[u] << 10) + ((unsigned)(ln ^ lat_swz(8 * c.wave + 4 * g + u)) << 4), u);
@@ -610,6 +621,20 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 
     // Score operands of the next chain, read ahead (kept across iterations).
     bf16x8 pre[kScDepth];
+    // Gather offsets of the next tile to fetch, computed during a mix (one
+    // per mix step, where independent MFMAs leave issue slots) and used by
+    // the next score chain.
+    unsigned goff[2][4];
+    u32x4 pv[2];
+    auto read_rows = [&](int tg) {
+        pv[0] = rows_index(tg, 0);
+        pv[1] = rows_index(tg, 1);
+    };
+    auto offsets_step = [&](int tg, int idx) {
+        const int gg = idx >> 2, u = idx & 3;
+        goff[gg][u] = row_offset(tg, pv[gg], gg, u);
+        asm volatile("" : "+v"(goff[gg][u]));
+    };
     auto preload = [&](int t) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
 #pragma unroll
@@ -635,8 +660,6 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         const float neg_m = have_ref ? -m_ref : 0.f;
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
-        const u32x4 pv[2] = {rows_index(t + 3, 0), rows_index(t + 3, 1)};
-        unsigned goff[2][4];
         bf16x8 pb[2];
         float psum = 0.f;
         f32x16 sacc;
@@ -652,19 +675,18 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             if (ks < 32 && !(ks & 1)) prob(scur, ks >> 1, sc, neg_m, pb, psum);
             if (ks == 32) close_sum(psum);
             if (ks == 33) store_p(pb);
-            if ((ks & 1) && ks < 16) {
-                // one gather offset per odd k-step (the even ones carry an
-                // exponential); the empty asm keeps it from being bunched up
-                const int gg = ks >> 3, u = (ks >> 1) & 3;
-                goff[gg][u] = row_offset(t + 3, pv[gg], gg, u);
-                asm volatile("" : "+v"(goff[gg][u]));
-            }
             if (ks == 18) issue_rows4(t + 3, 0, goff[0]);
             if (ks == 26) issue_rows4(t + 3, 1, goff[1]);
         }
         barrier_lds();                   // every head's probabilities of tile t in LDS
-        mix(t, [&](int idx) { if (idx == 7) hand_over(t + 2); },
-               [&](int idx) { if (idx == 3) gather_pe(t + 3, pidx); });
+        mix(t, [&](int idx) {
+                   if (idx == 0) read_rows(t + 4);
+                   if (idx == 7) hand_over(t + 2);
+               },
+               [&](int idx) {
+                   if (idx == 3) gather_pe(t + 3, pidx);
+                   offsets_step(t + 4, idx);
+               });
     };
     // Last tile: softmax and mix only.
     auto last = [&](int t, f32x16& scur) {
@@ -697,6 +719,9 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     f32x16 sA, sB;
     scores(0, sA);
     if (ntiles > 1) hand_over(1);
+    read_rows(3);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) offsets_step(3, idx);
     int t = 0;
     for (; t + 1 < ntiles; ++t) {
         body(t, sA, sB);

@@ -19,9 +19,11 @@ constexpr int kQRow = kLatent + kRope;  // 576: absorbed query row [q_c | q_pe]
 // and at most kMaxSlotsPerSplit slots.
 constexpr int kTileRows = 32;
 constexpr int kMaxSlotsPerSplit = 1024;
-// Largest cache length: gathers address one query's cache with 32-bit byte
-// offsets that must stay below 2^31.
-constexpr int kMaxT = (1 << 21) - 1;
+// Largest cache length.  Gathers address one query's latent cache with 32-bit
+// byte offsets against a buffer descriptor that covers T KiB plus a 3 KiB
+// prefix; an empty slot carries the offset 2^31, which must lie past that
+// range for every instruction offset: T*1024 + 3072 <= 2^31.
+constexpr int kMaxT = (1 << 21) - 4;
 
 // Workspace carve-up, shared by the size query and the launchers.
 struct Workspace {
