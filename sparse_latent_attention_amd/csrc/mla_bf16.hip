@@ -478,9 +478,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         // combine the two, moving the condition between the units
         unsigned lim_t = t < ntiles ? lim : 0u;
         asm volatile("" : "+s"(lim_t));
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // keep the per-row lane offsets out of the loop
-        return x4_off(pv[u] < lim_t, (pv[u] << 10) + ((unsigned)(ln ^ lat_swz(8 * c.wave + 4 * g + u)) << 4), u);
+        return x4_off(pv[u] < lim_t, (pv[u] << 10) + ((unsigned)(lane ^ lat_swz(8 * c.wave + 4 * g + u)) << 4), u);
     };
     auto issue_rows4 = [&](int t, int g, const unsigned (&v)[4]) {
         load_lds16_x4(c.kv_desc, tiles_addr + (t & (kBufs - 1)) * kBufBytes + (8 * c.wave + 4 * g) * 1024,
