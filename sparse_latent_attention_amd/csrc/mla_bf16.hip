@@ -532,10 +532,14 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // from the first tile with a selected slot.  Returns the score multiplier
     // to use (1 once masking has applied the scale).
     bool have_ref = false;
-    auto prepare = [&](int t, f32x16& s) -> float {
-        const int pv = c.sidx[t * kRows + j];
+    // Read once: inside the loop the compiler would reload it from the
+    // kernel arguments every tile (the assembly blocks clobber memory), and a
+    // scalar load is waited for together with every LDS read in flight.
+    const float scale_log2 = c.a->scale_log2;
+    // `pv` is this lane's index list entry of tile t (row j), read ahead.
+    auto prepare = [&](int t, f32x16& s, int pv) -> float {
         const unsigned vmask = (unsigned)__builtin_amdgcn_ballot_w64((unsigned)pv < lim);
-        float sc = c.a->scale_log2;
+        float sc = scale_log2;
         if (vmask != 0xFFFFFFFFu) {
             // this lane's rows are 8*(i/4) + 4*hsel + i%4
             const unsigned vml = vmask >> (4 * hsel);
@@ -643,9 +647,14 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // gathers of tile tn landed (the tile after it may stay in flight), then
     // a barrier after which tile tn is complete and every wave is done
     // reading the mixed tile and P.
+    // This lane's index entry of the tile whose softmax comes next (read
+    // ahead of the operand reads, so that waiting for it does not wait for
+    // them).
+    int sel = c.sidx[j];
     auto hand_over = [&](int tn) {
         MLA_WAIT_VMCNT(9);
         barrier_lds();
+        sel = c.sidx[(tn - 1) * kRows + j];
         preload(tn);
         asm volatile("" ::: "memory");   // issue the reads here, not at their first use
     };
@@ -654,7 +663,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // read ahead): scores of t+1 into snext, softmax of t from scur, gather
     // of t+3, then the mix of t, with the hand-over to iteration t+1.
     auto body = [&](int t, f32x16& scur, f32x16& snext) {
-        const float sc = prepare(t, scur);
+        const float sc = prepare(t, scur, sel);
         const float neg_m = have_ref ? -m_ref : 0.f;
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
@@ -688,7 +697,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     };
     // Last tile: softmax and mix only.
     auto last = [&](int t, f32x16& scur) {
-        const float sc = prepare(t, scur);
+        const float sc = prepare(t, scur, sel);
         const float neg_m = have_ref ? -m_ref : 0.f;
         bf16x8 pb[2];
         float psum = 0.f;
