@@ -511,7 +511,8 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         return *(const __attribute__((address_space(3))) bf16x8*)(tiles + ((pe_base + bo) ^ ((ks - 32) << 5)));
     };
     // Standalone score chain (first tile).
-    auto scores = [&](int t, f32x16& out) {
+    // Standalone score chain (first tile); side(ks) runs after each MFMA.
+    auto scores = [&](int t, f32x16& out, auto&& side) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
         f32x16 sacc;
         bf16x8 pre[kScDepth];
@@ -524,6 +525,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             if (ks == 0) mfma32_v_first(sacc, av, qf[0]);
             else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
             else mfma32_v_last(out, sacc, av, qf[ks]);
+            side(ks);
         }
     };
 
@@ -715,16 +717,22 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // The first score chain needs the query fragments and tile 0 only.  The
     // wait for them is a full one: the compiler does not see the gathers
     // (inline assembly), so after a partial wait it would still take the
-    // later query loads for pending and wait again inside the chain, on
-    // counts that include the gathers of tiles 1 and 2.  Those two go out
-    // once the wait is over.
+    // later query loads for pending and wait again inside the first score
+    // chain, on counts that include the gathers of tiles 1 and 2.  Those go
+    // out during that chain, spread over its k-steps rather than back to
+    // back, so that its MFMAs cover their issue.
     gather_tile(0);
     __builtin_amdgcn_s_waitcnt(0);
-    gather_tile(1);
-    gather_tile(2);
     barrier_only();
     f32x16 sA, sB;
-    scores(0, sA);
+    scores(0, sA, [&](int ks) {
+        if (ks == 2) gather_rows4(1, 0);
+        if (ks == 8) gather_rows4(1, 1);
+        if (ks == 14) gather_pe(1, gather_index(1));
+        if (ks == 20) gather_rows4(2, 0);
+        if (ks == 26) gather_rows4(2, 1);
+        if (ks == 32) gather_pe(2, gather_index(2));
+    });
     if (ntiles > 1) hand_over(1);
     read_rows(3);
 #pragma unroll
