@@ -950,8 +950,10 @@ __device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h
 
 // Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31; `lds` holds kUvLds
 // bytes (1 KiB aligned).  Every thread of the workgroup calls it.
+template <bool kLoadW>
 __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__ out, int h, int rb,
-                                         const bf16x8 (&wa)[32], unsigned char* lds) {
+                                         bf16x8 (&wa)[32], unsigned char* lds,
+                                         const __bf16* __restrict__ w_uv) {
     unsigned char* stage = lds;
     float* s_mmax = reinterpret_cast<float*>(lds + kUvStage);
     float* s_inv = s_mmax + kUvRows;
@@ -1050,12 +1052,16 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     };
 
     if (n_split <= kUvGroup) {
-        // Every split fits in LDS at once.  Each wave loads rows 8w .. 8w+7
-        // of every split, split by split, and each split is multiplied by
-        // W_UV as soon as it has landed while the later ones are in flight;
-        // the products are combined with the merge weights in float32 (the
-        // product is linear in O~).  The per-split maxima and sums are loaded
-        // first, so that they are the oldest loads in flight.
+        // Every split fits in LDS at once.  Each wave fetches rows 8w .. 8w+7
+        // of every split with plain 16-byte loads (a run of LDS-direct load
+        // groups would go one group at a time per wave, as each group's M0
+        // must stay put until it lands) and writes them to LDS, two splits
+        // at a time.  Order of the loads: the per-split maxima and sums, the
+        // first two splits, W_UV (on the first block), the other two splits,
+        // so that every wait the compiler places for a register counts only
+        // loads issued after it.  The products run split by split as the
+        // data lands and are combined with the merge weights in float32 (the
+        // product is linear in O~).
         const int rr_m = rb * kUvRows + mj;
         const bool have = rr_m < R && msub < n_split;
         float m0 = -INFINITY, l0 = 0.f;
@@ -1064,41 +1070,48 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
             l0 = a.l_part[o];
             m0 = a.m_part[o];
         }
-        {
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const unsigned row_bytes = kHeads * kLatent * 2;
-            for (int sp = 0; sp < n_split; ++sp) {
-                const __bf16* src0 = o_ws + (((size_t)sp * R + rb * kUvRows) * kHeads + h) * kLatent;
-                const u32x4 desc = make_desc_x4(src0, (unsigned)min(R - rb * kUvRows, kUvRows) * row_bytes);
+        // rows of one split as a buffer (rows past R read zeros, no branch)
+        const unsigned row_bytes = kHeads * kLatent * 2;
+        const int rows_here = min(R - rb * kUvRows, kUvRows);
+        auto load_rows = [&](int sp, u32x4 (&v)[8]) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+                o_ws + (((size_t)sp * R + rb * kUvRows) * kHeads + h) * kLatent, (unsigned)rows_here * row_bytes);
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int j0 = 8 * wave + 4 * g;
-                    unsigned v[4];
+            for (int r8 = 0; r8 < 8; ++r8)
+                v[r8] = buf_load16(rs, (unsigned)(8 * wave + r8) * row_bytes + 16u * lane);
+        };
+        auto store_rows = [&](int sp, const u32x4 (&v)[8]) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int jj = j0 + u;
-                        const bool ok = rb * kUvRows + jj < R;
-                        v[u] = x4_off(ok, (unsigned)jj * row_bytes +
-                                              (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(jj))) << 4), u);
-                    }
-                    load_lds16_x4(desc, stage_addr + (sp * kUvRows + j0) * 1024, v[0], v[1], v[2], v[3]);
-                }
+            for (int r8 = 0; r8 < 8; ++r8) {
+                const int jj = 8 * wave + r8;
+                *reinterpret_cast<u32x4*>(stage + (sp * kUvRows + jj) * 1024 +
+                                          (((lane & ~15) | ((lane & 15) ^ lat_swz(jj))) << 4)) = v[r8];
             }
-        }
+        };
         f32x16 part[kUvGroup];
-#pragma unroll
-        for (int sl = 0; sl < kUvGroup; ++sl) {
-            if (sl >= n_split) break;
-            // own loads of split sl done: the later splits' 8 each may remain
-            switch (n_split - 1 - sl) {
-                case 0: MLA_WAIT_VMCNT(0); break;
-                case 1: MLA_WAIT_VMCNT(8); break;
-                case 2: MLA_WAIT_VMCNT(16); break;
-                default: MLA_WAIT_VMCNT(24); break;
-            }
-            barrier_only();                  // every wave's rows of split sl landed
-            part[sl] = uv_product(sl);
+        {
+            u32x4 v0[8], v1[8];
+            load_rows(0, v0);
+            if (n_split > 1) load_rows(1, v1);
+            if (kLoadW) uv_load_w(w_uv, h, wa);
+            store_rows(0, v0);
+            if (n_split > 1) store_rows(1, v1);
+        }
+        barrier_lds();                       // splits 0 and 1 of every wave in LDS
+        if (n_split > 2) {
+            u32x4 v2[8], v3[8];
+            load_rows(2, v2);
+            if (n_split > 3) load_rows(3, v3);
+            part[0] = uv_product(0);
+            part[1] = uv_product(1);
+            store_rows(2, v2);
+            if (n_split > 3) store_rows(3, v3);
+            barrier_lds();                   // splits 2 and 3 in LDS
+            part[2] = uv_product(2);
+            if (n_split > 3) part[3] = uv_product(3);
+        } else {
+            part[0] = uv_product(0);
+            if (n_split > 1) part[1] = uv_product(1);
         }
         // merge weights: lane msub of row mj holds split msub's (m, l)
         float mloc = -INFINITY, wloc = 0.f;
@@ -1246,8 +1259,16 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __re
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvLds];
     const int h = blockIdx.x;
     bf16x8 wa[32];
-    uv_load_w(w_uv, h, wa);
-    for (int rb = blockIdx.y; rb * kUvRows < a.R; rb += r_groups) uv_block(a, out, h, rb, wa, lds);
+    // With at most kUvGroup splits the first block loads W_UV itself, after
+    // its first partial rows; otherwise W_UV is loaded here, once.
+    int rb = blockIdx.y;
+    if (a.n_split <= kUvGroup) {
+        uv_block<true>(a, out, h, rb, wa, lds, w_uv);
+        rb += r_groups;
+    } else {
+        uv_load_w(w_uv, h, wa);
+    }
+    for (; rb * kUvRows < a.R; rb += r_groups) uv_block<false>(a, out, h, rb, wa, lds, w_uv);
 }
 
 }  // namespace
