@@ -59,6 +59,16 @@ def ws_expected(rows, esize, n_split):
     return up(up(up(q) + o) + ml)
 
 
+def test_cache_length_limit(lib):
+    hdr = open(HDR).read()
+    max_t = int(re.search(r"#define MLA_MAX_T (\d+)", hdr).group(1))
+    # an empty slot's offset (2^31) must lie past the latent rows plus a 3 KiB prefix
+    assert max_t * 1024 + 3072 <= 2 ** 31
+    assert lib.mla_sparse_decode_workspace_size(1, max_t, 64, 1) > 0
+    assert lib.mla_sparse_decode_workspace_size(1, max_t + 1, 64, 1) == 0
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4, max_t + 1, 64, 1) == 0
+
+
 def test_workspace_size_plan(lib):
     # 64 rows: 4 splits of 512 slots fill the 256 compute units
     assert lib.mla_sparse_decode_workspace_size(64, 32768, 2048, 1) == ws_expected(64, 2, 4)

@@ -248,3 +248,41 @@ def test_moderate_scale(mla):
     out = to_host64(run_decode(mla, upload(inp), softmax_scale=0.5))
     ref = oracle.decode(inp, rows=[0, 7], scale=0.5)
     assert rel_err(out[[0, 7]], ref) <= TOL["bf16"]
+
+
+def _max_t() -> int:
+    """MLA_MAX_T as the public header defines it."""
+    import pathlib
+    import re
+    hdr = (pathlib.Path(__file__).resolve().parent.parent / "include" / "mla_sparse.h").read_text()
+    return int(re.search(r"#define MLA_MAX_T (\d+)", hdr).group(1))
+
+
+def test_largest_cache_length(mla):
+    """One batch row at T = MLA_MAX_T: selected rows at both ends of the cache (byte offsets
+    up to ~2^31), empty slots and an index equal to T among them, every other row NaN.
+    Decode has no causal mask, so the oracle sees the same rows packed into a short cache."""
+    T = _max_t()
+    kv_sel = 93                                  # selected rows; + 3 empty slots = 96 (3 tiles)
+    cfg = DecodeConfig(21, "maxT", B=1, T=kv_sel, k=kv_sel, dtype="bf16")
+    inp = synth.decode_inputs(cfg)               # every position of the short cache selected
+    rng = np.random.default_rng(7)
+    pos = np.sort(np.concatenate([[0, 1, T - 2, T - 1],
+                                  rng.choice(np.arange(2, T - 2), size=kv_sel - 4, replace=False)]))
+    log(f"decode at T={T}: {kv_sel} rows, last at byte offset {int(pos[-1]) * 1024}")
+    dev = upload({k: v for k, v in inp.items() if k not in ("kv_cache", "pe_cache", "topk_idx")})
+    big_kv = torch.full((1, T, 512), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    big_pe = torch.full((1, T, 64), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    pos_t = torch.from_numpy(pos).to("cuda:0")
+    big_kv[0, pos_t] = to_dev(inp["kv_cache"][0])
+    big_pe[0, pos_t] = to_dev(inp["pe_cache"][0])
+    idx = np.concatenate([pos, [-1, T, -1]]).astype(np.int32)   # T itself selects nothing
+    idx = rng.permutation(idx)[None, :]
+    got = to_host64(mla.decode(dev["q_nope"], dev["q_pe"], big_kv, big_pe,
+                               torch.from_numpy(idx).to("cuda:0"), dev["w_uk"], dev["w_uv"]))
+    torch.cuda.synchronize()
+    del big_kv, big_pe
+    assert np.all(np.isfinite(got))
+    err = rel_err(got, oracle.decode(inp))
+    log(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
