@@ -47,6 +47,8 @@ def parse():
                    help="untimed steps first: clocks and address translation need tens of ms of load to settle")
     p.add_argument("--sets", type=int, default=8, help="independently seeded query sets to rotate")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-mall-flush", action="store_true",
+                   help="skip the extra pass that writes a 512 MiB buffer before every call")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="batch rows timed on the CPU oracle (0 = size to ~15 s)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -150,31 +152,77 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int, command: str):
     print(json.dumps(rec, indent=1))
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, rows_wanted: int):
-    """Time the fp64 oracle on whole batch rows of the same workload (set 0)."""
+    """Time the fp64 oracle on whole batch rows of the same workload (set 0).
+
+    Returns the baseline object (the explicit form the oracle defines, all host threads)
+    and two more timings, labelled apart: the absorbed fp64 form on the selected rows
+    (the GPU's algorithm on the CPU) and the explicit form on one thread."""
     import oracle
     import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
+        threadpool_limits = None
         cores = os.cpu_count() or 1
     w_uk, w_uv = synth.weights(cfg)
+    rows = {}
 
-    def one(b):
-        kv, pe = synth.decode_batch_row(cfg, b)
-        qn, qp, idx = synth.decode_query_set(cfg, b, 0)
+    def inputs(b):
+        if b not in rows:
+            kv, pe = synth.decode_batch_row(cfg, b)
+            qn, qp, idx = synth.decode_query_set(cfg, b, 0)
+            rows[b] = (qn, qp, kv, pe, idx)
+        return rows[b]
+
+    def explicit(b):
+        qn, qp, kv, pe, idx = inputs(b)
         t0 = time.perf_counter()
         oracle.attend_explicit_gather(qn, qp, kv, pe, w_uk, w_uv, idx)
         return time.perf_counter() - t0
 
-    first = one(0)
+    def absorbed(b):
+        qn, qp, kv, pe, idx = inputs(b)
+        t0 = time.perf_counter()
+        oracle.decode_absorbed(qn, qp, kv[idx], pe[idx], w_uk, w_uv, np.arange(len(idx)))
+        return time.perf_counter() - t0
+
+    first = explicit(0)
     n = rows_wanted if rows_wanted > 0 else max(1, min(cfg.B, int(15.0 / max(first, 1e-3))))
-    spent = first + sum(one(b) for b in range(1, n))
-    return {"value": n * cfg.k / spent, "unit": "selected KV positions/s", "cores": int(cores),
+    spent = first + sum(explicit(b) for b in range(1, n))
+    model = _cpu_model()
+    base = {"value": n * cfg.k / spent, "unit": "selected KV positions/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{n} of {cfg.B} batch rows x {cfg.k} selected positions, explicit fp64 "
-                      f"form, {spent:.1f} s"}
+                      f"form, {spent:.1f} s on {model}"}
+    t_abs = sum(absorbed(b) for b in range(n))
+    extra = {"cpu_baseline_absorbed": {
+        "value": n * cfg.k / t_abs, "unit": "selected KV positions/s", "cores": int(cores),
+        "kind": "oracle absorbed form",
+        "sample": f"{n} of {cfg.B} batch rows x {cfg.k} selected positions, absorbed fp64 form "
+                  f"on the selected rows, {t_abs:.1f} s"}}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one = explicit(0)
+            m = max(1, min(n, int(10.0 / max(one, 1e-3))))
+            t1 = one + sum(explicit(b) for b in range(1, m))
+        extra["cpu_baseline_1thread"] = {
+            "value": m * cfg.k / t1, "unit": "selected KV positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{m} of {cfg.B} batch rows x {cfg.k} selected positions, explicit fp64 "
+                      f"form, one thread, {t1:.1f} s"}
+    return base, extra
 
 
 def main():
@@ -283,6 +331,34 @@ def main():
     for e in flat:
         hip.hipEventDestroy(e)
     attn_avg_ms = float(np.mean(attn_ms))
+    attn_pct = [float(np.percentile(attn_ms, q)) for q in (10, 50, 90)]
+
+    # pass 3: a 512 MiB write before every call evicts the 256 MB last-level
+    # cache; each call is bracketed by events after its write (median)
+    flushed_ms = None
+    if not args.no_mall_flush:
+        n_flush = min(args.steps, 100)
+        scratch = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        fev = device_events(hip, 2 * n_flush)
+        torch.cuda.synchronize()
+        for i in range(n_flush):
+            scratch.fill_(i & 255)
+            if hip.hipEventRecord(fev[2 * i], stream) != 0:
+                raise RuntimeError("hipEventRecord failed")
+            step(args.warmup + i)
+            if hip.hipEventRecord(fev[2 * i + 1], stream) != 0:
+                raise RuntimeError("hipEventRecord failed")
+        torch.cuda.synchronize()
+        per = []
+        for i in range(n_flush):
+            t = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(t), fev[2 * i], fev[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            per.append(t.value)
+        for e in fev:
+            hip.hipEventDestroy(e)
+        flushed_ms = float(np.median(per))
+        del scratch
 
     units = B * k
     achieved = units * ROW_BYTES / (attn_avg_ms * 1e-3) / 1e9
@@ -309,6 +385,8 @@ def main():
                    "B": B, "T": T, "k": k, "heads": 128, "parallelism": "none (1 GPU)"},
         "step_roofline_frac": t_roof_ms / ms,
         "attention_kernel_ms": attn_avg_ms,
+        "attention_kernel_ms_p10_p50_p90": attn_pct,
+        "ms_per_step_mall_flushed": flushed_ms,
         "ms_per_step_with_attention_events": ms_events,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
@@ -324,7 +402,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
+        base, extra = cpu_baseline(cfg, args.cpu_rows)
+        result["cpu_baseline"] = base
+        result.update(extra)
     print(json.dumps(result), flush=True)
 
 
