@@ -397,9 +397,9 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // Query fragments (B operands): head 32*wave + lane%32, columns
     // 16*ks + 8*(lane/32) .. +7.  Retiring their loads here leaves vmcnt
     // counting the gathers only inside the tile loop.
-    // Prologue, one memory round trip: the split's index list, the query
-    // fragments and (once the list is in LDS) the first three tiles are all in
-    // flight together.
+    // Prologue: the split's index list and the query fragments are in flight
+    // together; tile 0 follows once the list is in LDS, and tiles 1 and 2 go
+    // out during tile 0's score chain.
     constexpr int kIdxPerThread = kMaxSlotsPerSplit / 256;
     int iv[kIdxPerThread];
 #pragma unroll
