@@ -260,11 +260,14 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
 //            registers); if any later score beats m by more than 32, which no
 //            realistic attention does, a fallback recomputes the split with
 //            the exact per-head maxima;
-//   mix      O~^T[c][h] += sum_j V^T[c][j] P^T[j][h] (v_mfma 32x32x16).  The
-//            score accumulator already holds P^T in the B-operand layout of the
-//            mix, provided MFMA k slot 4t + e of lane half g is row
-//            16kc + 8t + 4g + e; V^T comes from the row-major tile through the
-//            transposing LDS read with the same slot order.
+//   mix      O~^T[c][h] += sum_j V^T[c][j] P^T[j][h] over all 512 columns c of
+//            the wave's own heads (v_mfma 32x32x16).  The probabilities, packed
+//            to bf16 where the score accumulator left them, already form the
+//            B operand of the mix, provided MFMA k slot 4t + e of lane half g
+//            is row 16kc + 8t + 4g + e; V^T comes from the row-major tile
+//            through the transposing LDS read with the same slot order.  So P
+//            never leaves registers and no wave waits for another between the
+//            softmax and the mix.
 // LDS tile layout: latent rows at 1024-byte stride with 16-byte chunk q of
 // row j stored at chunk q ^ swz(j); rotary rows in four 8-row blocks (1152-byte
 // stride) with chunk c of block row j' at c ^ j'.  Both the score reads and the
@@ -277,7 +280,6 @@ constexpr int kBufs = 4;                     // tile buffers
 constexpr int kLatBytes = kRows * 1024;
 constexpr int kPeBlock = 1152;               // 8 rotary rows (1 KiB) + 128-byte pad
 constexpr int kBufBytes = kLatBytes + 4 * kPeBlock;
-constexpr int kPRow = 80;                    // P^T staging row: 32 bf16 + 16-byte pad (one head)
 
 // Workgroup barrier after this wave's LDS writes have completed.  Written as
 // assembly with a memory clobber so that the compiler keeps LDS accesses on
@@ -360,7 +362,6 @@ __device__ __forceinline__ u32x4 make_desc_x4(const void* base, unsigned bytes) 
 struct SplitCtx {
     const AttnArgs* a;
     unsigned char* tiles;        // kBufs tile buffers in LDS (generic pointer to LDS)
-    unsigned char* pbuf;         // probabilities of one tile, [head][slot order], kPRow per head
     int* sidx;                   // the split's index list in LDS (-1 past its end)
     const int32_t* idx_src;      // the split's index list in global memory
     int nslots;                  // its length
@@ -376,6 +377,14 @@ struct SplitCtx {
 #define MLA_SC_DEPTH 6
 #endif
 constexpr int kScDepth = MLA_SC_DEPTH;
+// V^T operands of the mix read ahead of their MFMA.  The hand-over barrier
+// sits before the last four MFMAs of a mix, and every read of the tile must
+// be issued ahead of it (the barrier then also certifies that they landed).
+#ifndef MLA_MIX_DEPTH
+#define MLA_MIX_DEPTH 4
+#endif
+constexpr int kMixDepth = MLA_MIX_DEPTH;
+static_assert(kMixDepth >= 3 && kMixDepth <= 8, "mix read-ahead out of range");
 
 // A head whose per-tile probability sum exceeds this (relative to its
 // reference) is recomputed exactly by the merge; below it, no probability or
@@ -572,54 +581,33 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         beaten = beaten || !(psum <= kBeatenSum);
     };
 
-    // The probabilities of a tile go through LDS: lane (head h, half g) holds
-    // rows 8a + 4g + b (a, b = 0..3), which sit in MFMA k slot 8g + 4(a%2) + b
-    // of k-step a/2 (the slot order of the transposing V reads below), so
-    // each lane writes four 8-byte runs and the mix reads 16 bytes per operand.
-    const lds_u8* pbuf = (const lds_u8*)c.pbuf;
-    auto store_p = [&](const bf16x8 (&pb)[2]) {
-        unsigned char* row = c.pbuf + (32 * c.wave + (lane & 31)) * kPRow + 16 * hsel;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const bf16x4 v = {pb[a >> 1][4 * (a & 1)], pb[a >> 1][4 * (a & 1) + 1],
-                              pb[a >> 1][4 * (a & 1) + 2], pb[a >> 1][4 * (a & 1) + 3]};
-            *reinterpret_cast<bf16x4*>(row + 32 * (a >> 1) + 8 * (a & 1)) = v;
-        }
-    };
-    // Mix of the wave's quarter of the latent columns for all 128 heads:
-    // O~^T[c][h] += V^T[c][j] P^T[j][h], c = 128*wave + 32*cbi + (0..31),
-    // h = 32*hb + (0..31); acc[4*cbi + hb].
-    auto mix = [&](int t, auto&& before, auto&& after) {
+    // Mix of the wave's own heads over all 512 latent columns, one tile:
+    // O~^T[c][h] += V^T[c][j] P^T[j][h], c = 32*cb + (0..31), acc[cb].  Lane
+    // (head h, half g) holds in pb[kc] the probabilities of rows
+    // 16kc + 8t + 4g + e (slot 4t + e), which is exactly its share of the
+    // B operand of k-step kc.  V^T is read kMixDepth MFMAs ahead; before(i)
+    // runs ahead of MFMAs 4i .. 4i+3 and after(i) behind them.  Every MFMA
+    // with its reads and hooks forms its own scheduling region, so that the
+    // compiler cannot bunch the independent work between two MFMAs.
+    auto mix = [&](int t, const bf16x8 (&pbm)[2], auto&& before, auto&& after) {
         const int bo = (t & (kBufs - 1)) * kBufBytes;
-        const int y = c.wave * 256;
-        auto v_read = [&](int idx) -> bf16x8 {      // idx = 4*kc + cbi
-            const int kc = idx >> 2, x = (idx & 3) << 6;
+        auto v_read = [&](int m) -> bf16x8 {      // m = 16*kc + cb
+            const int kc = m >> 4, cb = m & 15;
+            const int x = (cb & 3) << 6, y = (cb >> 2) * 256;
             return cat(lds_read_tr(tiles + (((tr_base[kc][0] + bo) ^ x) + y)),
                        lds_read_tr(tiles + (((tr_base[kc][1] + bo) ^ x) + y)));
         };
-        auto p_read = [&](int hb, int kc) -> bf16x8 {
-            return *(const __attribute__((address_space(3))) bf16x8*)(
-                pbuf + (32 * hb + (lane & 31)) * kPRow + 32 * kc + 16 * hsel);
-        };
-        bf16x8 pk[2][4];
-        bf16x8 va[2];
+        bf16x8 va[kMixDepth];
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) pk[0][hb] = p_read(hb, 0);
-        va[0] = v_read(0);
+        for (int d = 0; d < kMixDepth; ++d) va[d] = v_read(d);
 #pragma unroll
-        for (int idx = 0; idx < 8; ++idx) {
-            if (idx + 1 < 8) va[(idx + 1) & 1] = v_read(idx + 1);
-            if (idx == 2)
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb) pk[1][hb] = p_read(hb, 1);
-            const int kc = idx >> 2, cbi = idx & 3;
-            before(idx);
-            // keep the last MFMAs below whatever before() issued
-            if (idx == 7) asm volatile("" : "+v"(va[1]));
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-                acc[4 * cbi + hb] = mfma32(va[idx & 1], pk[kc][hb], acc[4 * cbi + hb]);
-            after(idx);
+        for (int m = 0; m < 32; ++m) {
+            const bf16x8 av = va[m % kMixDepth];
+            if (m + kMixDepth < 32) va[m % kMixDepth] = v_read(m + kMixDepth);
+            if ((m & 3) == 0) before(m >> 2);
+            acc[m & 15] = mfma32(av, pbm[m >> 4], acc[m & 15]);
+            if ((m & 3) == 3) after(m >> 2);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -648,7 +636,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // so that they cover the latency of the next chain's first reads: own
     // gathers of tile tn landed (the tile after it may stay in flight), then
     // a barrier after which tile tn is complete and every wave is done
-    // reading the mixed tile and P.
+    // reading the mixed tile.
     // This lane's index entry of the tile whose softmax comes next (read
     // ahead of the operand reads, so that waiting for it does not wait for
     // them).
@@ -680,15 +668,15 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             else if (ks < 35) mfma32_v(sacc, av, qf[ks]);
             else mfma32_v_last(snext, sacc, av, qf[ks]);
             // one exponential every other k-step, so that each fits in the
-            // shadow of the MFMA in flight
+            // shadow of the MFMA in flight; each k-step is a scheduling
+            // region of its own, or the compiler bunches the exponentials
             if (ks < 32 && !(ks & 1)) prob(scur, ks >> 1, sc, neg_m, pb, psum);
             if (ks == 32) close_sum(psum);
-            if (ks == 33) store_p(pb);
             if (ks == 18) issue_rows4(t + 3, 0, goff[0]);
             if (ks == 26) issue_rows4(t + 3, 1, goff[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        barrier_lds();                   // every head's probabilities of tile t in LDS
-        mix(t, [&](int idx) {
+        mix(t, pb, [&](int idx) {
                    if (idx == 0) read_rows(t + 4);
                    if (idx == 7) hand_over(t + 2);
                },
@@ -706,9 +694,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 #pragma unroll
         for (int i = 0; i < 16; ++i) prob(scur, i, sc, neg_m, pb, psum);
         close_sum(psum);
-        store_p(pb);
-        barrier_lds();
-        mix(t, [](int) {}, [](int) {});
+        mix(t, pb, [](int) {}, [](int) {});
     };
 
 #pragma unroll
@@ -747,10 +733,10 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 }
 
 // Write this split's normalised bf16 mix (+ reference and sum).  Each wave
-// holds a quarter of the columns of every head; the sums live with the waves
-// that computed the heads' scores, so they go through LDS first.  Rows are
-// staged in LDS (the tile buffers are free by now) and every head row is
-// written with one 1 KiB store instruction.
+// holds all 512 columns of its own 32 heads (a head's columns split between
+// lanes l and l ^ 32).  Rows are staged in LDS (the tile buffers are free once
+// every wave is done with them) and every head row is written with one 1 KiB
+// store instruction.
 constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (spreads banks)
 
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
@@ -758,29 +744,20 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     const AttnArgs& a = *c.a;
     const int lane = c.lane;
     const float l_tot = l_run + __shfl_xor(l_run, 32);   // a head spans lanes l and l ^ 32
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h_own = 32 * c.wave + (lane & 31);
-    float* inv_l = reinterpret_cast<float*>(c.pbuf);
-    barrier_only();                                      // every wave is done with tiles and P
-    if (lane < 32) inv_l[h_own] = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    barrier_lds();
-    float inv[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) inv[hb] = inv_l[32 * hb + (lane & 31)];
+    barrier_only();                                      // every wave is done with the tiles
 
-    // acc[4*cbi + hb] element i: head 32hb + lane%32, column
-    // 128*wave + 32*cbi + 8*(i/4) + 4*(lane/32) + i%4.
-    unsigned char* mine = c.tiles + (lane & 31) * kOutRow + (128 * c.wave + 4 * (lane >> 5)) * 2;
+    // acc[cb] element i: head h_own, column 32*cb + 8*(i/4) + 4*(lane/32) + i%4.
+    unsigned char* mine = c.tiles + h_own * kOutRow + 8 * (lane >> 5);
 #pragma unroll
-    for (int cbi = 0; cbi < 4; ++cbi)
+    for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x16& v = acc[4 * cbi + hb];
-                *reinterpret_cast<bf16x4*>(mine + 32 * hb * kOutRow + 64 * cbi + 16 * gq) =
-                    to_bf16x4(v[4 * gq] * inv[hb], v[4 * gq + 1] * inv[hb], v[4 * gq + 2] * inv[hb],
-                              v[4 * gq + 3] * inv[hb]);
-            }
+        for (int gq = 0; gq < 4; ++gq) {
+            const f32x16& v = acc[cb];
+            *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
+                to_bf16x4(v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv);
+        }
     barrier_lds();
     __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
     const unsigned char* stage = c.tiles + 32 * c.wave * kOutRow;
@@ -804,13 +781,12 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
 // read from HBM once.  Latest query rows (most work) go first.  Returns false
 // for a slot past the last row.
 __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& a, int id, unsigned char* tiles,
-                                           unsigned char* pbuf, int* sidx) {
+                                           int* sidx) {
     const int split = (id >> 3) % a.n_split;
     const int rr = ((id >> 3) / a.n_split) * 8 + (id & 7);
     if (rr >= a.R) return false;
     c.a = &a;
     c.tiles = tiles;
-    c.pbuf = pbuf;
     c.sidx = sidx;
     c.r = (a.R - 1) - rr;
     c.split = split;
@@ -831,15 +807,15 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& a, int i
     return true;
 }
 
-// LDS of the attention pass: tile buffers, one tile's probabilities, the split's index list.
+// LDS of the attention pass: tile buffers and the split's index list.
 constexpr int kAttnTilesLds = kBufs * kBufBytes;
-constexpr int kAttnLds = kAttnTilesLds + kHeads * kPRow + kMaxSlotsPerSplit * 4;
+constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4;
+static_assert(kHeads * kOutRow <= kAttnTilesLds, "output staging must fit in the tile buffers");
 
 __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttnLds];
     SplitCtx c;
-    if (!attn_setup(c, a, blockIdx.x, lds, lds + kAttnTilesLds,
-                    reinterpret_cast<int*>(lds + kAttnTilesLds + kHeads * kPRow)))
+    if (!attn_setup(c, a, blockIdx.x, lds, reinterpret_cast<int*>(lds + kAttnTilesLds)))
         return;
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
