@@ -31,9 +31,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -732,11 +729,13 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     MLA_WAIT_VMCNT(0);                   // no gather may land after the workgroup ends
 }
 
-// Write this split's normalised bf16 mix (+ reference and sum).  Each wave
-// holds all 512 columns of its own 32 heads (a head's columns split between
-// lanes l and l ^ 32).  Rows are staged in LDS (the tile buffers are free once
-// every wave is done with them) and every head row is written with one 1 KiB
-// store instruction.
+// Write this split's mix in bf16, not normalised (+ reference and sum; the
+// merge divides by the total sum, so the normalisation costs no work here,
+// where it would be 256 multiplies per lane at the end of the kernel).  Each
+// wave holds all 512 columns of its own 32 heads (a head's columns split
+// between lanes l and l ^ 32).  Rows are staged in LDS (the tile buffers are
+// free once every wave is done with them) and every head row is written with
+// one 1 KiB store instruction.
 constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (spreads banks)
 
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
@@ -744,7 +743,6 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     const AttnArgs& a = *c.a;
     const int lane = c.lane;
     const float l_tot = l_run + __shfl_xor(l_run, 32);   // a head spans lanes l and l ^ 32
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int h_own = 32 * c.wave + (lane & 31);
     barrier_only();                                      // every wave is done with the tiles
 
@@ -756,7 +754,7 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
         for (int gq = 0; gq < 4; ++gq) {
             const f32x16& v = acc[cb];
             *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
-                to_bf16x4(v[4 * gq] * inv, v[4 * gq + 1] * inv, v[4 * gq + 2] * inv, v[4 * gq + 3] * inv);
+                to_bf16x4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
         }
     barrier_lds();
     __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
@@ -835,8 +833,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) 
 // Each 32-row block of O~ is built in LDS: the split partials of up to four
 // splits at a time are loaded straight into LDS (latent chunk c of row j at
 // the same swizzled position as in the attention tiles), merged in float32
-// with weights w_s = l_s 2^(m_s - max) / sum, and written back as bf16 into
-// the first split's rows, which then feed the MFMA B operand.
+// with weights w_s = 2^(m_s - max) / sum_s' l_s' 2^(m_s' - max) (the partials
+// are not normalised), and written back as bf16 into the first split's rows,
+// which then feed the MFMA B operand.
 // --------------------------------------------------------------------------
 constexpr int kUvRows = 32;
 constexpr int kUvGroup = 4;                    // splits staged in LDS at a time
@@ -945,7 +944,6 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     const int wave = wave_id();
     const int lane = tid & 63;
     const int half = lane >> 5;
-    const int d = 32 * wave + (lane & 31);
     const unsigned stage_addr = (unsigned)(size_t)stage;
     const __bf16* o_ws = reinterpret_cast<const __bf16*>(a.o);
 
@@ -975,9 +973,10 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     // Merge weight of a split with reference m and sum l for a row with
     // maximum mm and inverse weight sum inv: l 2^(m - mm) inv; a split with no
     // selected slot (l = 0) or an inexact one (l < 0) weighs 0.
+    // Weight of a split's (unnormalised) partial: 2^(m - mm) / (sum over the
+    // splits of l 2^(m - mm)), with inv that sum's inverse.
     auto weight = [&](float m, float l, float mm, float inv) {
-        const float w = n_split == 1 ? 1.f : l * exp2f(m - mm) * inv;
-        return l > 0.f ? w : 0.f;
+        return l > 0.f ? exp2f(m - mm) * inv : 0.f;
     };
 
 

@@ -44,7 +44,7 @@ Workspace plan_workspace(int rows, int k, int dtype) {
     w.q_off = 0;
     w.q_bytes = R * kHeads * kQRow * esize;
     w.o_off = round_up(w.q_off + w.q_bytes, kAlign);
-    // bf16: per split, the normalised mix in bf16 + reference max and sum
+    // bf16: per split, the unnormalised mix in bf16 + reference max and sum
     // (a negative sum marks a head the merge must recompute exactly);
     // f32: per split, the unnormalised mix in f32 + running max and sum.
     const bool bf16 = dtype == MLA_BF16;
