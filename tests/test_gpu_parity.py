@@ -123,6 +123,27 @@ def test_prefill_from_position_zero_all_rows(mla):
 
 
 # ------------------------------------------------------------------ edge cases
+
+def _bf16_decode_workspace(rows, k, n_split):
+    """Workspace bytes of a bf16 decode of `rows` query rows split into n_split splits."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    q = rows * 128 * 576 * 2
+    o = n_split * rows * 128 * 512 * 2
+    ml = 2 * n_split * rows * 128 * 4
+    return up(up(up(q) + o) + ml)
+
+
+@pytest.mark.parametrize("B,k,n_split", [(64, 32, 1), (64, 64, 2), (64, 96, 3), (64, 128, 4),
+                                         (52, 160, 5)])
+def test_split_counts(mla, B, k, n_split):
+    # Every split count from one to five: one split (the merge only divides by
+    # the sum), the paths that stage up to four splits at once with their
+    # partial-count branches, and the grouped path past four.
+    assert mla.decode_workspace_size(B, 900, k, torch.bfloat16) == _bf16_decode_workspace(B, k, n_split)
+    check_decode(mla, DecodeConfig(40 + n_split, f"splits{n_split}", B=B, T=900, k=k, dtype="bf16"),
+                 rows=[0, 1, B // 2, B - 1])
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_single_selected_row(mla, dtype):
     check_decode(mla, DecodeConfig(14, "k1", B=2, T=50, k=1, dtype=dtype))
