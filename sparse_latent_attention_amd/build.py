@@ -25,6 +25,11 @@ FLAGS = [
     "-fvisibility=hidden",
     # packed fp32 vector ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into scalar registers: the leading scalar
+    # parameters of each kernel (up to the 16 registers the hardware allows)
+    # are there when a workgroup starts, so its first loads do not wait for a
+    # kernel-argument load
+    "-mllvm", "-amdgpu-kernarg-preload-count=11",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

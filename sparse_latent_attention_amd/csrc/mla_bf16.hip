@@ -254,9 +254,9 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
 //   softmax  per lane, in the log2 domain, against a reference m taken from
 //            the head's first tile with a selected row: p = 2^(s - m).  The
 //            accumulator is never rescaled (which keeps it in the accumulation
-//            registers); if any later score beats m by more than 32, which no
-//            realistic attention does, a fallback recomputes the split with
-//            the exact per-head maxima;
+//            registers); if a head's probabilities in one tile sum past 2^32
+//            (a later score beat m by about 32), which no realistic attention
+//            does, the head is flagged and the merge recomputes it exactly;
 //   mix      O~^T[c][h] += sum_j V^T[c][j] P^T[j][h] over all 512 columns c of
 //            the wave's own heads (v_mfma 32x32x16).  The probabilities, packed
 //            to bf16 where the score accumulator left them, already form the
@@ -774,16 +774,31 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     }
 }
 
+// The arguments a workgroup needs before its first loads.  The attention and
+// merge kernels take them as leading scalar parameters, which the build has
+// the compiler preload into scalar registers (-amdgpu-kernarg-preload-count):
+// a workgroup then issues its first loads without first waiting for a
+// kernel-argument load.  The full argument block follows them for everything
+// needed later.
+struct AttnEarly {
+    const void* kv;
+    const void* pe;
+    const int32_t* idx;
+    const void* q;
+    int R, T, k, n_split, slots_per_split, causal_base;
+    long long cache_rows_per_query;
+};
+
 // Workgroup slot -> (query row, split).  Consecutive slots land on the 8 XCDs
 // in turn; the splits of one query row share an XCD, so its absorbed query is
 // read from HBM once.  Latest query rows (most work) go first.  Returns false
 // for a slot past the last row.
-__device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& a, int id, unsigned char* tiles,
-                                           int* sidx) {
+__device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, const AttnEarly& a, int id,
+                                           unsigned char* tiles, int* sidx) {
     const int split = (id >> 3) % a.n_split;
     const int rr = ((id >> 3) / a.n_split) * 8 + (id & 7);
     if (rr >= a.R) return false;
-    c.a = &a;
+    c.a = &args;
     c.tiles = tiles;
     c.sidx = sidx;
     c.r = (a.R - 1) - rr;
@@ -810,10 +825,14 @@ constexpr int kAttnTilesLds = kBufs * kBufBytes;
 constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4;
 static_assert(kHeads * kOutRow <= kAttnTilesLds, "output staging must fit in the tile buffers");
 
-__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a, int row_groups) {
+__global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* pe, const int32_t* idx,
+                                                    const void* q, int R, int T, int k, int n_split,
+                                                    int slots_per_split, int causal_base,
+                                                    long long cache_rows_per_query, AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttnLds];
     SplitCtx c;
-    if (!attn_setup(c, a, blockIdx.x, lds, reinterpret_cast<int*>(lds + kAttnTilesLds)))
+    const AttnEarly early{kv, pe, idx, q, R, T, k, n_split, slots_per_split, causal_base, cache_rows_per_query};
+    if (!attn_setup(c, a, early, blockIdx.x, lds, reinterpret_cast<int*>(lds + kAttnTilesLds)))
         return;
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
@@ -923,10 +942,19 @@ __device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h
     for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
 }
 
+// The merge kernel's counterpart of AttnEarly: what a workgroup needs before
+// its first loads, passed as leading scalar parameters.
+struct UvEarly {
+    const __bf16* o;
+    const float* m_part;
+    const float* l_part;
+    int R, n_split;
+};
+
 // Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31; `lds` holds kUvLds
 // bytes (1 KiB aligned).  Every thread of the workgroup calls it.
 template <bool kLoadW>
-__device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__ out, int h, int rb,
+__device__ __forceinline__ void uv_block(const AttnArgs& a, const UvEarly& e, __bf16* __restrict__ out, int h, int rb,
                                          bf16x8 (&wa)[32], unsigned char* lds,
                                          const __bf16* __restrict__ w_uv) {
     unsigned char* stage = lds;
@@ -938,14 +966,14 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     float* xred = xo + kLatent;
     float* xp = xred + 4;
     int* xpos = reinterpret_cast<int*>(xp + 256);
-    const int R = a.R;
-    const int n_split = a.n_split;
+    const int R = e.R;
+    const int n_split = e.n_split;
     const int tid = threadIdx.x;
     const int wave = wave_id();
     const int lane = tid & 63;
     const int half = lane >> 5;
     const unsigned stage_addr = (unsigned)(size_t)stage;
-    const __bf16* o_ws = reinterpret_cast<const __bf16*>(a.o);
+    const __bf16* o_ws = e.o;
 
     // Partial rows (split g0 + wave, query row rb*32 + j) -> staged row
     // (wave, j); rows past R or splits past n_split load zeros.
@@ -1042,8 +1070,8 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
         float m0 = -INFINITY, l0 = 0.f;
         if (have) {
             const size_t o = ((size_t)msub * R + rr_m) * kHeads + h;
-            l0 = a.l_part[o];
-            m0 = a.m_part[o];
+            l0 = e.l_part[o];
+            m0 = e.m_part[o];
         }
         // rows of one split as a buffer (rows past R read zeros, no branch)
         const unsigned row_bytes = kHeads * kLatent * 2;
@@ -1137,8 +1165,8 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
             if (rr < R) {
                 for (int sp = msub; sp < n_split; sp += 8) {
                     const size_t o = ((size_t)sp * R + rr) * kHeads + h;
-                    const float l = a.l_part[o];
-                    const float m = a.m_part[o];
+                    const float l = e.l_part[o];
+                    const float m = e.m_part[o];
                     if (sp == msub) {
                         m0 = m;
                         l0 = l;
@@ -1186,7 +1214,7 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
                     float w = 0.f;
                     if (rr < R && g0 + sl < n_split) {
                         const size_t o = ((size_t)(g0 + sl) * R + rr) * kHeads + h;
-                        w = weight(a.m_part[o], a.l_part[o], s_mmax[j], s_inv[j]);
+                        w = weight(e.m_part[o], e.l_part[o], s_mmax[j], s_inv[j]);
                     }
                     s_w[sl][j] = w;
                 }
@@ -1229,21 +1257,23 @@ __device__ __forceinline__ void uv_block(const AttnArgs& a, __bf16* __restrict__
     }
 }
 
-__global__ __launch_bounds__(256, 1) void uv_bf16(AttnArgs a, const __bf16* __restrict__ w_uv,
-                                                  __bf16* __restrict__ out, int r_groups) {
+__global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* o, const float* m_part, const float* l_part,
+                                                  const __bf16* __restrict__ w_uv, int R, int n_split,
+                                                  int r_groups, __bf16* __restrict__ out, AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvLds];
+    const UvEarly early{o, m_part, l_part, R, n_split};
     const int h = blockIdx.x;
     bf16x8 wa[32];
     // With at most kUvGroup splits the first block loads W_UV itself, after
     // its first partial rows; otherwise W_UV is loaded here, once.
     int rb = blockIdx.y;
-    if (a.n_split <= kUvGroup) {
-        uv_block<true>(a, out, h, rb, wa, lds, w_uv);
+    if (n_split <= kUvGroup) {
+        uv_block<true>(a, early, out, h, rb, wa, lds, w_uv);
         rb += r_groups;
     } else {
         uv_load_w(w_uv, h, wa);
     }
-    for (; rb * kUvRows < a.R; rb += r_groups) uv_block<false>(a, out, h, rb, wa, lds, w_uv);
+    for (; rb * kUvRows < R; rb += r_groups) uv_block<false>(a, early, out, h, rb, wa, lds, w_uv);
 }
 
 }  // namespace
@@ -1262,15 +1292,18 @@ hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* 
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
     const int row_groups = (a.R + 7) / 8;
-    hipLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, a, row_groups);
+    hipLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, a.kv, a.pe, a.idx, a.q,
+                       a.R, a.T, a.k, a.n_split, a.slots_per_split, a.causal_base, a.cache_rows_per_query,
+                       a);
     return hipGetLastError();
 }
 
 hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s) {
     const int blocks = (a.R + 31) / 32;
     const int r_groups = blocks < 8 ? blocks : 8;
-    hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, a,
-                       static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(out), r_groups);
+    hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, static_cast<const __bf16*>(a.o),
+                       a.m_part, a.l_part, static_cast<const __bf16*>(w_uv), a.R, a.n_split, r_groups,
+                       static_cast<__bf16*>(out), a);
     return hipGetLastError();
 }
 
