@@ -11,11 +11,12 @@ before.
 Prints one JSON line.  `value` is selected KV positions per second (B * k per
 step), from a timed pass of K steps with nothing but the steps on the stream.
 `roofline` covers the attention kernel: a second timed pass runs the same K
-steps with HIP events recorded on the launch stream right before and after the
-attention kernel of every step (event records add a few microseconds to the
-steps they bracket, which is why they stay out of the first pass).  The events
-use a device-scope release (hipEventReleaseToDevice).  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload.
+steps with a start and a stop HIP event on the attention kernel of every step,
+timestamped by that kernel's own dispatch on its stream (the library launches
+it with hipExtLaunchKernel), so each interval is the kernel's duration.  The
+events still add about a microsecond per step, which is why they stay out of
+the first pass; they use a device-scope release (hipEventReleaseToDevice).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -322,7 +323,7 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
 
-    # pass 2: the same steps, attention kernel bracketed by events
+    # pass 2: the same steps, each attention kernel timed by its own dispatch's events
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):

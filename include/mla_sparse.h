@@ -137,11 +137,13 @@ MLA_API mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int
                          int* d_flag, hipStream_t stream);
 
 /*
- * Timing hook.  When `begin` and `end` are non-NULL, the next decode or
- * prefill call records `begin` on its stream immediately before its attention
- * kernel and `end` immediately after it, then forgets both.  Passing NULLs
- * cancels a pending request.  Process-wide, not thread-safe; intended for
- * benchmarks.
+ * Timing hook.  When `begin` and `end` are non-NULL (events the caller has
+ * created, with timing enabled), the next decode or prefill call has the
+ * dispatch of its attention kernel record `begin` when the kernel starts and
+ * `end` when it completes (hipExtLaunchKernel), then forgets both: their
+ * interval is the kernel's own duration, without the cost of separate event
+ * records.  Passing NULLs cancels a pending request.  Process-wide, not
+ * thread-safe; intended for benchmarks.
  */
 MLA_API mla_status mla_set_attention_events(hipEvent_t begin, hipEvent_t end);
 

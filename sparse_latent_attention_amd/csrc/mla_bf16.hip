@@ -18,6 +18,8 @@
 // columns c + 4q .. c + 4q + 3 of a row-major bf16 matrix, lane i of the
 // block receives column c + i of rows r_0 .. r_3: a column-major MFMA operand
 // read from row-major storage.
+#include <hip/hip_ext.h>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -25,7 +27,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -1290,11 +1291,11 @@ hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* 
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int row_groups = (a.R + 7) / 8;
-    hipLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, a.kv, a.pe, a.idx, a.q,
-                       a.R, a.T, a.k, a.n_split, a.slots_per_split, a.causal_base, a.cache_rows_per_query,
-                       a);
+    hipExtLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, start, stop, 0,
+                          a.kv, a.pe, a.idx, a.q, a.R, a.T, a.k, a.n_split, a.slots_per_split, a.causal_base,
+                          a.cache_rows_per_query, a);
     return hipGetLastError();
 }
 

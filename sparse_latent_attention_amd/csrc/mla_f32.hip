@@ -1,5 +1,7 @@
 // float32 kernels: the same five steps in plain float32 vector arithmetic
 // (no reduced-precision operands anywhere), plus the index-list validator.
+#include <hip/hip_ext.h>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -187,8 +189,8 @@ hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w
     return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(attn_f32, dim3(kHeads, a.n_split, a.R), dim3(256), 0, s, a);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL(attn_f32, dim3(kHeads, a.n_split, a.R), dim3(256), 0, s, start, stop, 0, a);
     return hipGetLastError();
 }
 

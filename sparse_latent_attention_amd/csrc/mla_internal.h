@@ -52,15 +52,19 @@ struct AttnArgs {
     float* l_part;          // [n_split, R, 128]
 };
 
-// Launchers (return hipSuccess or the launch error).
+// Launchers (return hipSuccess or the launch error).  The attention launchers
+// take optional start and stop events, which the kernel's dispatch itself
+// timestamps (hipExtLaunchKernel): the interval is the kernel's own duration.
 hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
                               int R, hipStream_t s);
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start = nullptr,
+                            hipEvent_t stop = nullptr);
 hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s);
 
 hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
                              int R, hipStream_t s);
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start = nullptr,
+                           hipEvent_t stop = nullptr);
 hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,
                          const void* w_uv, void* out, int R, int n_split, hipStream_t s);
 

@@ -93,10 +93,8 @@ mla_status run(const void* q_nope, const void* q_pe, const void* kv_cache, const
 
     hipEvent_t eb = g_attn_begin, ee = g_attn_end;
     g_attn_begin = g_attn_end = nullptr;
-    if (eb && hipEventRecord(eb, stream) != hipSuccess) return MLA_ERR_HIP;
-    e = dtype == MLA_BF16 ? launch_attn_bf16(a, stream) : launch_attn_f32(a, stream);
+    e = dtype == MLA_BF16 ? launch_attn_bf16(a, stream, eb, ee) : launch_attn_f32(a, stream, eb, ee);
     if (e != hipSuccess) return MLA_ERR_HIP;
-    if (ee && hipEventRecord(ee, stream) != hipSuccess) return MLA_ERR_HIP;
 
     if (dtype == MLA_BF16)
         e = launch_uv_bf16(a, w_uv, out, stream);
