@@ -389,11 +389,12 @@ static_assert(kMixDepth >= 3 && kMixDepth <= 8, "mix read-ahead out of range");
 // partial sum comes near the float/bf16 range.
 constexpr float kBeatenSum = 4294967296.f;   // 2^32
 
-// One pass over the split's tiles.  Software pipeline, per iteration t:
-//   wait for tile t+1, barrier, then the score MFMAs of tile t+1 run with the
-//   softmax of tile t and the gather of tile t+3 interleaved between them
-//   (VALU and memory instructions issue while an MFMA executes), then the mix
-//   MFMAs of tile t.
+// One pass over the split's tiles.  Software pipeline, per iteration t: the
+// score MFMAs of tile t+1 run with the softmax of tile t and the gathers of
+// tile t+3 interleaved between them (VALU and memory instructions issue while
+// an MFMA executes), then the mix MFMAs of tile t, with the hand-over to the
+// next iteration (own gathers of tile t+2 landed, then a barrier) before its
+// last four MFMAs.
 // The reference of each head is the (scaled) maximum of its first tile with
 // a selected row; no rescaling happens afterwards.  `beaten` reports a tile
 // whose probabilities exceeded kBeatenSum against that reference.
