@@ -112,15 +112,20 @@ __device__ __forceinline__ size_t q_off(int r, int h, int c) {
 // query row.  Workgroup = (head, quarter of c, group of 32-row query blocks).
 // The weight slice [128 d x 128 c] is staged in LDS with 16-byte loads and
 // read back transposed; wave w keeps the fragments of its 32 columns in
-// registers for every query block it visits.  The first block's queries are
-// loaded together with the weight (one memory round trip), and each output
-// block goes through LDS so that every row segment (128 c = 256 bytes) is
-// written by 16 consecutive lanes.
+// registers for every query block it visits.  A query block (32 rows x 128 d)
+// is the B operand of all four waves: the workgroup loads it once (32 bytes
+// per thread), stages it in LDS and each wave reads its fragments from there.
+// The first two blocks are loaded together with the weight (one memory round
+// trip), and each output block goes through LDS so that every row segment
+// (128 c = 256 bytes) is written by 16 consecutive lanes.
 // --------------------------------------------------------------------------
 constexpr int kWRow = 320;   // bytes per staged W_UK row (128 bf16 + pad)
 constexpr int kQcRow = 272;  // bytes per staged output row (128 bf16 + pad)
 
-constexpr int kAbsorbLds = kNope * kWRow + 32 * kQcRow;   // LDS one absorb unit uses
+constexpr int kQnRow = 272;  // bytes per staged query row (128 bf16 + pad)
+
+// LDS one absorb unit uses: the weight slice, one output block, two query blocks
+constexpr int kAbsorbLds = kNope * kWRow + 32 * kQcRow + 2 * 32 * kQnRow;
 
 // One unit = (head h, quarter cq of the 512 latent columns), for query blocks
 // rb_first, rb_first + rb_step, ...; `lds` holds kAbsorbLds bytes.  Every
@@ -132,6 +137,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
                                             int rb_first, int r_groups, unsigned char* lds) {
     unsigned char* wbuf = lds;
     unsigned char* obuf = lds + kNope * kWRow;
+    unsigned char* qbuf[2] = {obuf + 32 * kQcRow, obuf + 32 * kQcRow + 32 * kQnRow};
     const int h = unit >> 2;
     const int cq = unit & 3;
     const int tid = threadIdx.x;
@@ -139,18 +145,31 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
     const int lane = tid & 63;
     const int half = lane >> 5;
 
-    // B fragments of one 32-row block: q_nope[r][h][16ks + 8half .. +7], r = lane % 32
-    auto load_q = [&](int rb, bf16x8 (&b)[8]) {
-        const int r = rb * 32 + (lane & 31);
+    // One 32-row query block: thread t fetches 32 bytes, row t/8, columns
+    // d = 16*(t%8) .. +15 (rows past R read as zeros), and stages them in LDS.
+    auto load_q = [&](int rb, u32x4 (&p)[2]) {
+        const int r = rb * 32 + (tid >> 3);
         const bool rv = r < R;
-        const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 8 * half;
+        const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 16 * (tid & 7);
+        p[0] = rv ? *reinterpret_cast<const u32x4*>(qn) : u32x4{};
+        p[1] = rv ? *reinterpret_cast<const u32x4*>(qn + 8) : u32x4{};
+    };
+    auto stage_q = [&](const u32x4 (&p)[2], unsigned char* qb) {
+        unsigned char* dst = qb + (tid >> 3) * kQnRow + 32 * (tid & 7);
+        *reinterpret_cast<u32x4*>(dst) = p[0];
+        *reinterpret_cast<u32x4*>(dst + 16) = p[1];
+    };
+    // B fragments of a staged block: q_nope[r][h][16ks + 8half .. +7], r = lane % 32
+    auto frags_q = [&](const unsigned char* qb, bf16x8 (&b)[8]) {
+        const unsigned char* src = qb + (lane & 31) * kQnRow + 16 * half;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) b[ks] = rv ? *reinterpret_cast<const bf16x8*>(qn + 16 * ks) : bf16x8{};
+        for (int ks = 0; ks < 8; ++ks) b[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
     };
     const int blocks = (R + 31) / 32;
     bf16x8 b0[8], b1[8];
-    load_q(rb_first, b0);
-    if (rb_first + r_groups < blocks) load_q(rb_first + r_groups, b1);
+    u32x4 p0[2], p1[2];
+    load_q(rb_first, p0);
+    if (rb_first + r_groups < blocks) load_q(rb_first + r_groups, p1);
 
     {
         // 128 rows d x 16 chunks of 8 columns; 8 chunks per thread
@@ -167,7 +186,11 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             *reinterpret_cast<u32x4*>(wbuf + (e >> 4) * kWRow + 16 * (e & 15)) = v[i];
         }
     }
+    stage_q(p0, qbuf[0]);
+    if (rb_first + r_groups < blocks) stage_q(p1, qbuf[1]);
     __syncthreads();
+    frags_q(qbuf[0], b0);
+    if (rb_first + r_groups < blocks) frags_q(qbuf[1], b1);
 
     // A fragments: W_UK[h][d][c] for c = 32*wave + lane%32 (within the quarter),
     // d = 16*ks + 8*half + e (e = 0..7) via two transposing reads.
@@ -212,13 +235,26 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
         }
         __syncthreads();                  // obuf reused by the next block
     };
-    // Two query blocks in flight: while one is multiplied, the next but one loads.
+    // Two query blocks in flight: while one is multiplied, the next but one
+    // loads; it is staged once every wave has its fragments of the block
+    // before (process ends with a barrier) and read back after the barrier
+    // below.
     for (int rb = rb_first; rb < blocks; rb += 2 * r_groups) {
+        const bool more0 = rb + 2 * r_groups < blocks;
+        const bool has1 = rb + r_groups < blocks;
+        const bool more1 = rb + 3 * r_groups < blocks;
+        if (more0) load_q(rb + 2 * r_groups, p0);
         process(rb, b0);
-        if (rb + 2 * r_groups < blocks) load_q(rb + 2 * r_groups, b0);
-        if (rb + r_groups < blocks) {
+        if (more0) stage_q(p0, qbuf[0]);
+        if (has1) {
+            if (more1) load_q(rb + 3 * r_groups, p1);
             process(rb + r_groups, b1);
-            if (rb + 3 * r_groups < blocks) load_q(rb + 3 * r_groups, b1);
+            if (more1) stage_q(p1, qbuf[1]);
+        }
+        if (more0) {
+            __syncthreads();              // staged blocks visible
+            frags_q(qbuf[0], b0);
+            if (more1) frags_q(qbuf[1], b1);
         }
     }
 }
