@@ -437,7 +437,8 @@ constexpr float kBeatenSum = 4294967296.f;   // 2^32
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
                                           float& l_run, bool& beaten) {
     const int lane = c.lane;
-    const int ntiles = c.ntiles;
+    // A slot is selected iff 0 <= p < lim (p < T and, for prefill, p <= limit).
+    const unsigned lim = min((unsigned)c.T, (unsigned)c.limit + 1u);
     // Query fragments (B operands): head 32*wave + lane%32, columns
     // 16*ks + 8*(lane/32) .. +7.  Retiring their loads here leaves vmcnt
     // counting the gathers only inside the tile loop.
@@ -454,12 +455,33 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     bf16x8 qf[36];
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 512 * ks);
+    // The split's last selected slot: tiles past it hold no selected row (a
+    // causal prefill query early in its chunk leaves most of its list empty)
+    // and are not processed.
+    int last_sel = -1;
 #pragma unroll
     for (int u = 0; u < kIdxPerThread; ++u) {
         const int i = (int)threadIdx.x + 256 * u;
-        if (i < ntiles * kRows) c.sidx[i] = iv[u];
+        if (i < c.nslots && (unsigned)iv[u] < lim) last_sel = i;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last_sel = max(last_sel, __shfl_xor(last_sel, o));
+    if (lane == 0) c.sidx[kMaxSlotsPerSplit + c.wave] = last_sel;
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = (int)threadIdx.x + 256 * u;
+        if (i < c.ntiles * kRows) c.sidx[i] = iv[u];
     }
     barrier_lds();
+    const int* wave_last = c.sidx + kMaxSlotsPerSplit;
+    const int ntiles = (max(max(wave_last[0], wave_last[1]), max(wave_last[2], wave_last[3])) + kRows) / kRows;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
+    l_run = 0.f;
+    if (ntiles == 0) {                   // nothing selected: an empty partial
+        __builtin_amdgcn_s_waitcnt(0);   // no load may land after the workgroup ends
+        return;
+    }
 
     // Per-lane LDS offsets, relative to a tile buffer.  Buffer offsets are
     // multiples of 512 bytes, so XOR-ing a compile-time constant into bits 5..7
@@ -485,8 +507,6 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             tr_base[kc][t] = row * 1024 + (e4 << 6) + ((lo ^ (2 * t + g)) << 4) + (q4 & 1) * 8;
         }
 
-    // A slot is selected iff 0 <= p < lim (p < T and, for prefill, p <= limit).
-    const unsigned lim = min((unsigned)c.T, (unsigned)c.limit + 1u);
     const lds_u8* tiles = (const lds_u8*)c.tiles;
     const unsigned tiles_addr = (unsigned)(size_t)c.tiles;
     const int jp = lane >> 3;                          // rotary row of this lane's gather
@@ -732,9 +752,6 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         mix(t, pb, [](int) {}, [](int) {});
     };
 
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-    l_run = 0.f;
     // The first score chain needs the query fragments and tile 0 only.  The
     // wait for them is a full one: the compiler does not see the gathers
     // (inline assembly), so after a partial wait it would still take the
@@ -858,9 +875,10 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, co
     return true;
 }
 
-// LDS of the attention pass: tile buffers and the split's index list.
+// LDS of the attention pass: tile buffers, the split's index list and each
+// wave's last selected slot.
 constexpr int kAttnTilesLds = kBufs * kBufBytes;
-constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4;
+constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4 + 4 * 4;   // + each wave's last selected slot
 static_assert(kHeads * kOutRow <= kAttnTilesLds, "output staging must fit in the tile buffers");
 
 __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* pe, const int32_t* idx,
