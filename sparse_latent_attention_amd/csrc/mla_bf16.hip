@@ -880,6 +880,7 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, co
 constexpr int kAttnTilesLds = kBufs * kBufBytes;
 constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4 + 4 * 4;   // + each wave's last selected slot
 static_assert(kHeads * kOutRow <= kAttnTilesLds, "output staging must fit in the tile buffers");
+static_assert(kAttnLds <= 160 * 1024, "attention LDS exceeds a compute unit's 160 KiB");
 
 __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* pe, const int32_t* idx,
                                                     const void* q, int R, int T, int k, int n_split,

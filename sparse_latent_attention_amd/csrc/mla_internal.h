@@ -18,7 +18,7 @@ constexpr int kQRow = kLatent + kRope;  // 576: absorbed query row [q_c | q_pe]
 // split of that row's index list; splits hold whole tiles of kTileRows slots
 // and at most kMaxSlotsPerSplit slots.
 constexpr int kTileRows = 32;
-constexpr int kMaxSlotsPerSplit = 1024;
+constexpr int kMaxSlotsPerSplit = 2048;
 // Largest cache length.  Gathers address one query's latent cache with 32-bit
 // byte offsets against a buffer descriptor that covers T KiB plus a 3 KiB
 // prefix; an empty slot carries the offset 2^31, which must lie past that

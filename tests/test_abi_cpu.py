@@ -77,10 +77,11 @@ def test_workspace_size_plan(lib):
     # one row, 1001 slots: splits capped by the 32-slot tile count
     assert lib.mla_sparse_decode_workspace_size(1, 1001, 1001, 1) == ws_expected(1, 2, 32)
     assert lib.mla_sparse_decode_workspace_size(1, 64, 64, 0) == ws_expected(1, 4, 2)
-    # 4096 queries: as few splits as possible; splits never exceed 1024 slots
+    # 4096 queries: as few splits as possible; splits never exceed 2048 slots
     assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 4096, 1024, 1) == ws_expected(4096, 2, 1)
-    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 4096, 2048, 1) == ws_expected(4096, 2, 2)
-    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 8192, 4096, 1) == ws_expected(4096, 2, 4)
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 4096, 2048, 1) == ws_expected(4096, 2, 1)
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 8192, 4096, 1) == ws_expected(4096, 2, 2)
+    assert lib.mla_sparse_prefill_chunk_workspace_size(4096, 8192, 4097, 1) == ws_expected(4096, 2, 3)
     # invalid arguments report zero
     assert lib.mla_sparse_decode_workspace_size(0, 10, 5, 1) == 0
     assert lib.mla_sparse_decode_workspace_size(1, 10, 11, 1) == 0
