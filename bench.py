@@ -37,7 +37,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROW_BYTES = 576 * 2            # one selected latent + rotary row, bf16
 ROW_FLOPS = 2 * 128 * 576 + 2 * 128 * 512   # scores + mix for 128 heads
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_latent_attention_amd", "csrc", "mla_bf16.hip")
+# The code that decides what the decode kernels read and write: the bf16 kernels, the shared
+# constants and the host-side work split.
+KERNEL_SOURCES = tuple(os.path.join(ROOT, "sparse_latent_attention_amd", "csrc", f)
+                       for f in ("mla_bf16.hip", "mla_internal.h", "mla_sparse.cpp"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic_b64_t32k_k2048.json")
 
 
@@ -60,6 +63,9 @@ def parse():
                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "this script with --copy-calibration-mib into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     p.add_argument("--traffic-command", default="", help="command line recorded with --write-traffic")
+    p.add_argument("--prefill", action="store_true",
+                   help="time the prefill chunk (S=T=4096, k=min(t+1, 2048), bf16) instead of decode; "
+                        "prints its own JSON line (not the headline metric)")
     return p.parse_args()
 
 
@@ -94,10 +100,10 @@ def device_events(hip, n):
 
 
 def source_hash(text=None) -> str:
-    """Hash of the kernel source's code: comments and blank space are dropped, so an edit
+    """Hash of the kernel sources' code: comments and blank space are dropped, so an edit
     to a comment keeps the counter record, and any change to the code voids it."""
     if text is None:
-        text = open(KERNEL_SOURCE).read()
+        text = "\n".join(open(p).read() for p in KERNEL_SOURCES)
     code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     code = re.sub(r"//[^\n]*", " ", code)
     code = " ".join(code.split())
@@ -234,6 +240,55 @@ def cpu_baseline(cfg, rows_wanted: int):
     return base, extra
 
 
+def bench_prefill(args, torch, synth, mla):
+    """One prefill chunk of one sequence: S = T = 4096 queries from position 0, query t
+    selecting min(t + 1, 2048) positions up to its own.  Throughput is the algorithmic FLOP of
+    the chunk (absorptions plus 278,528 FLOP per selected (query, position) pair) per second."""
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS["prefill_s4096"]
+    inp = synth.prefill_inputs(cfg)
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype in (np.int32, np.int64):
+            return torch.from_numpy(x).to(dev)
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    d = {name: up(v) for name, v in inp.items()}
+    S, k = cfg.S, cfg.k
+    pairs = int((d["topk_idx"] >= 0).sum().item())
+    flop = pairs * ROW_FLOPS + 2 * 2 * S * 128 * 128 * 512
+    out = torch.empty((S, 128, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.prefill_chunk_workspace_size(S, cfg.T, k, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    steps = min(args.steps, 50)
+    warm = min(args.warmup, 10)
+
+    def call():
+        mla.prefill_chunk(d["q_nope"], d["q_pe"], d["kv_cache"], d["pe_cache"], d["topk_idx"],
+                          d["w_uk"], d["w_uv"], start_pos=cfg.start_pos, out=out, workspace=ws)
+
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / steps
+    tflops = flop / sec / 1e12
+    print(json.dumps({
+        "metric": "prefill chunk FLOP/s (S=T=4096, k=min(t+1,2048))", "value": flop / sec,
+        "unit": "FLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic prefill_s4096 inputs",
+        "config": {"workload": "prefill chunk S=4096, T=4096, k=min(t+1, 2048), 128 heads, bf16",
+                   "pairs": pairs, "flop": flop},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -254,6 +309,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     mla._lib.load()
+    if args.prefill:
+        bench_prefill(args, torch, synth, mla)
+        return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS["sparse_b64_t32k"]
     B, T, k = cfg.B, cfg.T, cfg.k

@@ -18,8 +18,10 @@ def test_source_hash_ignores_comments_and_blank_space():
     assert len(bench.source_hash(code)) == 16
 
 
-def test_source_hash_of_the_kernel_file_is_stable():
-    text = open(bench.KERNEL_SOURCE).read()
+def test_source_hash_of_the_kernel_files_is_stable():
+    assert [os.path.basename(p) for p in bench.KERNEL_SOURCES] == ["mla_bf16.hip", "mla_internal.h",
+                                                                  "mla_sparse.cpp"]
+    text = "\n".join(open(p).read() for p in bench.KERNEL_SOURCES)
     assert bench.source_hash() == bench.source_hash(text)
     assert bench.source_hash(text + "\n// trailing note\n") == bench.source_hash(text)
 
@@ -66,7 +68,7 @@ def test_traffic_record_is_used_only_while_the_code_matches(tmp_path, monkeypatc
     src = tmp_path / "kernel.hip"
     src.write_text("int kernel() { return 1; }\n")
     rec_file = tmp_path / "traffic.json"
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", (str(src),))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec_file))
     assert bench.traffic_from_profile(1) is None            # no record
     rec_file.write_text(json.dumps({"kernel_source_sha256_16": bench.source_hash(),
