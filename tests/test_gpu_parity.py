@@ -158,6 +158,24 @@ def test_empty_slots_and_empty_selection(mla):
     assert np.array_equal(out[1], np.zeros((128, 128)))
 
 
+def test_trailing_empty_tiles_are_skipped(mla):
+    # 64 rows and k = 512: four splits of 128 slots, four tiles each.  A split runs its tiles
+    # up to its last selected slot only, and a split with none selected writes an empty
+    # partial; lists that end early, or hold a single slot, exercise both.
+    cfg = DecodeConfig(18, "tails", B=64, T=2000, k=512, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    idx = inp["topk_idx"]
+    idx[0, 1:] = -1            # one slot: split 0 runs one tile, splits 1-3 are empty
+    idx[1, 33:] = -1           # split 0 runs two tiles
+    idx[2, 200:] = -1          # split 1 ends inside its third tile; splits 2 and 3 are empty
+    idx[3, :-1] = -1           # only the last slot: split 3 runs all four tiles, the rest none
+    keep = idx[4, 130]
+    idx[4, :] = -1
+    idx[4, 130] = keep         # one slot inside split 1's first tile
+    idx[5, 64:128] = -1        # split 0 ends after two tiles; splits 1-3 are full
+    check_decode(mla, cfg, rows=[0, 1, 2, 3, 4, 5, 63], inp=inp)
+
+
 def test_unselected_rows_never_read(mla):
     cfg = DecodeConfig(16, "poison", B=2, T=500, k=90, dtype="bf16")
     inp = synth.decode_inputs(cfg)
