@@ -233,6 +233,44 @@ def test_empty_selection_reads_as_zero_output():
     assert np.array_equal(out, np.zeros((H, DV)))
 
 
+# ---------------------------------------------------------------- batched decode
+def decode_batch_case(seed=14, B=3, T=20, k=7):
+    """B batch rows, each with its own cache, queries and index list."""
+    rng = np.random.default_rng(seed)
+    lat = rng.standard_normal((B, T, DL))
+    lat /= np.sqrt(np.mean(lat * lat, axis=2, keepdims=True))
+    return {"q_nope": rng.standard_normal((B, H, DN)), "q_pe": rng.standard_normal((B, H, DR)),
+            "kv_cache": lat, "pe_cache": rng.standard_normal((B, T, DR)),
+            "topk_idx": np.stack([np.sort(rng.choice(T, k, replace=False)) for _ in range(B)]),
+            "w_uk": rng.standard_normal((H, DN, DL)) / np.sqrt(512),
+            "w_uv": rng.standard_normal((H, DV, DL)) / np.sqrt(512)}
+
+
+def test_D1_batched_decode_pairs_rows_and_honours_scale():
+    # The batched entry point every decode parity check uses: batch row b's queries meet
+    # row b's own cache and index list ("Mix and project", decode-branch code: one query per
+    # sequence, scores against that sequence's cache), under the caller's scale.  Each row
+    # is compared with torch's CPU SDPA on keys and values built from the definition.
+    inp = decode_batch_case()
+    scale = 0.7
+    rows = [2, 0]
+    got = om.decode(inp, rows=rows, scale=scale)
+    assert got.shape == (2, H, DV)
+    for i, b in enumerate(rows):
+        ref = sdpa_reference(inp["q_nope"][b], inp["q_pe"][b], inp["kv_cache"][b],
+                             inp["pe_cache"][b], inp["w_uk"], inp["w_uv"], inp["topk_idx"][b],
+                             scale=scale)
+        assert rel_err(got[i], ref) <= 1e-12
+    full = om.decode(inp, rows=rows, scale=scale, gather=False)
+    assert rel_err(full, got) <= 1e-12
+    # default rows: every batch row, in order; default scale 1/sqrt(192)
+    every = om.decode(inp)
+    assert every.shape == (3, H, DV)
+    ref1 = sdpa_reference(inp["q_nope"][1], inp["q_pe"][1], inp["kv_cache"][1], inp["pe_cache"][1],
+                          inp["w_uk"], inp["w_uv"], inp["topk_idx"][1])
+    assert rel_err(every[1], ref1) <= 1e-12
+
+
 # ---------------------------------------------------------------- prefill pins
 def prefill_case(T, S, start_pos, seed, k):
     qn0, qp0, lat, rope, w_uk, w_uv = rand_case(T, seed)
@@ -290,8 +328,9 @@ def test_prefill_ignores_listed_positions_beyond_the_query():
 
 
 # ---------------------------------------------------------------- mutations
-def _pins_all_pass():
-    """Run the value pins; return the names of those that fail."""
+def _pins_all_pass(stop_at_first=False):
+    """Run the value pins; return the names of those that fail (only the first one with
+    ``stop_at_first``)."""
     failed = []
     for name, fn in [("I1", test_I1_absorbed_scores_equal_explicit_scores),
                      ("I3", test_I3_all_positions_selected_equals_unmasked_attention),
@@ -300,11 +339,14 @@ def _pins_all_pass():
                      ("C3", test_C3_identity_weights_reduce_to_textbook_attention),
                      ("C4", test_C4_dense_case_matches_library_attention),
                      ("P1", test_prefill_full_causal_equals_library_causal_attention),
-                     ("P3", test_prefill_ignores_listed_positions_beyond_the_query)]:
+                     ("P3", test_prefill_ignores_listed_positions_beyond_the_query),
+                     ("D1", test_D1_batched_decode_pairs_rows_and_honours_scale)]:
         try:
             fn()
         except AssertionError:
             failed.append(name)
+            if stop_at_first:
+                break
     return failed
 
 
@@ -328,6 +370,19 @@ MUTATIONS = {
     # causal bound off by one (query cannot see itself)
     "causal_off_by_one": ("index_mask", lambda orig: (
         lambda T, idx, lim=None: orig(T, idx, None if lim is None else lim - 1))),
+    # batched decode pairs row b's queries with the next row's cache and index list
+    "decode_row_pairing": ("decode", lambda orig: (
+        lambda inp, rows=None, gather=True, scale=SCALE: orig(
+            dict(inp, kv_cache=np.roll(inp["kv_cache"], 1, axis=0),
+                 pe_cache=np.roll(inp["pe_cache"], 1, axis=0),
+                 topk_idx=np.roll(inp["topk_idx"], 1, axis=0)), rows=rows, gather=gather,
+            scale=scale))),
+    # batched decode ignores the caller's scale
+    "decode_drops_scale": ("decode", lambda orig: (
+        lambda inp, rows=None, gather=True, scale=SCALE: orig(inp, rows=rows, gather=gather))),
+    # batched decode ignores the requested rows and returns every batch row
+    "decode_ignores_rows": ("decode", lambda orig: (
+        lambda inp, rows=None, gather=True, scale=SCALE: orig(inp, gather=gather, scale=scale))),
 }
 
 
@@ -342,7 +397,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, make = MUTATIONS[name]
     orig = getattr(om, attr)
     monkeypatch.setattr(om, attr, make(orig))
-    failed = _pins_all_pass()
+    failed = _pins_all_pass(stop_at_first=True)
     assert failed, f"mutation {name} slipped past every pin"
 
 
