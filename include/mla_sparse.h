@@ -137,6 +137,25 @@ MLA_API mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int
                          int* d_flag, hipStream_t stream);
 
 /*
+ * Diagnostics of the last decode or prefill call that used `workspace`, with
+ * the same row count (B or S), k and dtype: copies, asynchronously on
+ * `stream`, the number of index-list splits that call's attention kernel ran
+ * a second time into *d_count (device int, caller-owned, 4-byte aligned).
+ *
+ * The softmax ("Mix and project" page, All 4 steps: A = softmax, O~ = A c^KV)
+ * is computed per split of an index list against a reference score per head,
+ * taken from the split's first tile of 32 positions with a selected one.
+ * When a later score beats that reference by about 60 in log2 units (so that
+ * the probabilities could leave the float range), the bf16 path discards the
+ * split's pass and runs it again: once to find each head's largest score,
+ * then in full with that as the reference.  Each rerun split counts one.
+ * The float32 path keeps a running maximum instead and reports 0.
+ * Off the hot path; the next call does not read it.
+ */
+MLA_API mla_status mla_read_rerun_count(const void* workspace, int rows, int k, int dtype,
+                                        int* d_count, hipStream_t stream);
+
+/*
  * Timing hook.  When `begin` and `end` are non-NULL (events the caller has
  * created, with timing enabled), the next decode or prefill call has the
  * dispatch of its attention kernel record `begin` when the kernel starts and

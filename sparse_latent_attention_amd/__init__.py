@@ -18,7 +18,8 @@ N_HEADS, D_LATENT, D_ROPE, D_NOPE, D_V = 128, 512, 64, 128, 128
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 
 __all__ = ["decode", "prefill_chunk", "decode_workspace_size", "prefill_chunk_workspace_size",
-           "validate_indices", "set_attention_events", "status_string", "abi_version",
+           "validate_indices", "rerun_count", "set_attention_events", "status_string",
+           "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
 
 
@@ -37,6 +38,32 @@ def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+class _on_stream:
+    """Run a call's preparation and launches on `stream` (default: the current stream).
+
+    With an explicit stream, that stream first waits for the work queued so far on the
+    current one (which produced the inputs), and the index conversion, the workspace and
+    a library-allocated output are made while it is current, so the caching allocator
+    ties them to the stream whose kernels use them.
+    """
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.ctx = None
+
+    def __enter__(self):
+        if self.stream is not None:
+            self.stream.wait_stream(torch.cuda.current_stream())
+            self.ctx = torch.cuda.stream(self.stream)
+            self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+        return False
 
 
 def _require(t: torch.Tensor, name: str, shape, dtype, device):
@@ -93,34 +120,35 @@ def decode(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, T=None,
     [B,ld_T,64], topk_idx [B,k] (int32/int64, <0 = empty slot), w_uk/w_uv
     [128,128,512].  T (default ld_T) is the number of valid cached positions.
     """
-    lib = _lib.load()
-    dt, dev = q_nope.dtype, q_nope.device
-    B = q_nope.shape[0]
-    ld_T = kv_cache.shape[1]
-    T = ld_T if T is None else int(T)
-    idx = _index32(topk_idx)
-    k = idx.shape[1]
-    _require(q_nope, "q_nope", (B, N_HEADS, D_NOPE), dt, dev)
-    _require(q_pe, "q_pe", (B, N_HEADS, D_ROPE), dt, dev)
-    _require(kv_cache, "kv_cache", (B, ld_T, D_LATENT), dt, dev)
-    _require(pe_cache, "pe_cache", (B, ld_T, D_ROPE), dt, dev)
-    _require(idx, "topk_idx", (B, k), torch.int32, dev)
-    _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
-    _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
-    if out is None:
-        out = torch.empty((B, N_HEADS, D_V), dtype=dt, device=dev)
-    _require(out, "out", (B, N_HEADS, D_V), dt, dev)
-    code = _dtype_code(dt)
-    need = lib.mla_sparse_decode_workspace_size(B, T, k, code)
-    if need == 0:
-        raise MLAError(2, "mla_sparse_decode_workspace_size")
-    ws = _workspace(need, dev, workspace)
-    st = lib.mla_sparse_decode(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
-                               _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), B, T, ld_T, k,
-                               float(softmax_scale), code, _ptr(ws),
-                               ws.numel() * ws.element_size(), _stream(stream))
-    _lib.check(st, "mla_sparse_decode")
-    return out
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = q_nope.dtype, q_nope.device
+        B = q_nope.shape[0]
+        ld_T = kv_cache.shape[1]
+        T = ld_T if T is None else int(T)
+        idx = _index32(topk_idx)
+        k = idx.shape[1]
+        _require(q_nope, "q_nope", (B, N_HEADS, D_NOPE), dt, dev)
+        _require(q_pe, "q_pe", (B, N_HEADS, D_ROPE), dt, dev)
+        _require(kv_cache, "kv_cache", (B, ld_T, D_LATENT), dt, dev)
+        _require(pe_cache, "pe_cache", (B, ld_T, D_ROPE), dt, dev)
+        _require(idx, "topk_idx", (B, k), torch.int32, dev)
+        _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
+        _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
+        if out is None:
+            out = torch.empty((B, N_HEADS, D_V), dtype=dt, device=dev)
+        _require(out, "out", (B, N_HEADS, D_V), dt, dev)
+        code = _dtype_code(dt)
+        need = lib.mla_sparse_decode_workspace_size(B, T, k, code)
+        if need == 0:
+            raise MLAError(2, "mla_sparse_decode_workspace_size")
+        ws = _workspace(need, dev, workspace)
+        st = lib.mla_sparse_decode(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
+                                   _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), B, T, ld_T, k,
+                                   float(softmax_scale), code, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+        _lib.check(st, "mla_sparse_decode")
+        return out
 
 
 def prefill_chunk(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, start_pos=0,
@@ -130,44 +158,57 @@ def prefill_chunk(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, sta
     kv_cache [T,512], pe_cache [T,64]; query s is at position start_pos + s and
     ignores listed positions beyond it; topk_idx [S,k] is -1 padded.
     """
-    lib = _lib.load()
-    dt, dev = q_nope.dtype, q_nope.device
-    S = q_nope.shape[0]
-    T = kv_cache.shape[0]
-    idx = _index32(topk_idx)
-    k = idx.shape[1]
-    _require(q_nope, "q_nope", (S, N_HEADS, D_NOPE), dt, dev)
-    _require(q_pe, "q_pe", (S, N_HEADS, D_ROPE), dt, dev)
-    _require(kv_cache, "kv_cache", (T, D_LATENT), dt, dev)
-    _require(pe_cache, "pe_cache", (T, D_ROPE), dt, dev)
-    _require(idx, "topk_idx", (S, k), torch.int32, dev)
-    _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
-    _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
-    if out is None:
-        out = torch.empty((S, N_HEADS, D_V), dtype=dt, device=dev)
-    _require(out, "out", (S, N_HEADS, D_V), dt, dev)
-    code = _dtype_code(dt)
-    need = lib.mla_sparse_prefill_chunk_workspace_size(S, T, k, code)
-    if need == 0:
-        raise MLAError(2, "mla_sparse_prefill_chunk_workspace_size")
-    ws = _workspace(need, dev, workspace)
-    st = lib.mla_sparse_prefill_chunk(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
-                                      _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), S, T, k,
-                                      int(start_pos), float(softmax_scale), code, _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(stream))
-    _lib.check(st, "mla_sparse_prefill_chunk")
-    return out
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = q_nope.dtype, q_nope.device
+        S = q_nope.shape[0]
+        T = kv_cache.shape[0]
+        idx = _index32(topk_idx)
+        k = idx.shape[1]
+        _require(q_nope, "q_nope", (S, N_HEADS, D_NOPE), dt, dev)
+        _require(q_pe, "q_pe", (S, N_HEADS, D_ROPE), dt, dev)
+        _require(kv_cache, "kv_cache", (T, D_LATENT), dt, dev)
+        _require(pe_cache, "pe_cache", (T, D_ROPE), dt, dev)
+        _require(idx, "topk_idx", (S, k), torch.int32, dev)
+        _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
+        _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
+        if out is None:
+            out = torch.empty((S, N_HEADS, D_V), dtype=dt, device=dev)
+        _require(out, "out", (S, N_HEADS, D_V), dt, dev)
+        code = _dtype_code(dt)
+        need = lib.mla_sparse_prefill_chunk_workspace_size(S, T, k, code)
+        if need == 0:
+            raise MLAError(2, "mla_sparse_prefill_chunk_workspace_size")
+        ws = _workspace(need, dev, workspace)
+        st = lib.mla_sparse_prefill_chunk(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
+                                          _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), S, T, k,
+                                          int(start_pos), float(softmax_scale), code, _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream))
+        _lib.check(st, "mla_sparse_prefill_chunk")
+        return out
 
 
 def validate_indices(topk_idx, T: int, allow_pad: bool = False, stream=None) -> int:
     """Run the library's index check; returns 0 (valid) or a bitmask (1 range, 2 repeat)."""
-    lib = _lib.load()
-    idx = _index32(topk_idx)
-    flag = torch.empty(1, dtype=torch.int32, device=idx.device)
-    st = lib.mla_validate_indices(_ptr(idx), idx.shape[0], idx.shape[1], int(T),
-                                  1 if allow_pad else 0, _ptr(flag), _stream(stream))
-    _lib.check(st, "mla_validate_indices")
-    return int(flag.item())
+    with _on_stream(stream):
+        lib = _lib.load()
+        idx = _index32(topk_idx)
+        flag = torch.empty(1, dtype=torch.int32, device=idx.device)
+        st = lib.mla_validate_indices(_ptr(idx), idx.shape[0], idx.shape[1], int(T),
+                                      1 if allow_pad else 0, _ptr(flag), _stream(stream))
+        _lib.check(st, "mla_validate_indices")
+        return int(flag.item())
+
+
+def rerun_count(workspace, rows: int, k: int, dtype: torch.dtype, stream=None) -> int:
+    """Index-list splits the last call that used ``workspace`` ran twice (softmax reference beaten)."""
+    with _on_stream(stream):
+        lib = _lib.load()
+        cnt = torch.empty(1, dtype=torch.int32, device=workspace.device)
+        st = lib.mla_read_rerun_count(_ptr(workspace), int(rows), int(k), _dtype_code(dtype),
+                                      _ptr(cnt), _stream(stream))
+        _lib.check(st, "mla_read_rerun_count")
+        return int(cnt.item())
 
 
 def set_attention_events(begin, end) -> None:

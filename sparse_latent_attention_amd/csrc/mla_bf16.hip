@@ -89,6 +89,22 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Combine the values of lanes l and l ^ 32 (v_permlane32_swap exchanges the
+// upper half of one register with the lower half of the other: swapping a
+// value with itself leaves, in the two results, the lower and the upper half
+// of the wave broadcast to both halves).  Needs no address register, unlike
+// a shuffle through ds_bpermute.
+__device__ __forceinline__ float pair_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
@@ -263,8 +279,9 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
                                                      const __bf16* __restrict__ q_pe,
                                                      const __bf16* __restrict__ w_uk,
                                                      __bf16* __restrict__ q_out, int R,
-                                                     int r_groups) {
+                                                     int r_groups, int* stats) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kAbsorbLds];
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *stats = 0;   // the call's diagnostics
     // Workgroups are dealt to the eight XCDs in turn (id % 8).  XCD x takes
     // heads 16x .. 16x+15 with all four column quarters, so a head's queries
     // come from memory once per launch (the other quarters hit that XCD's L2)
@@ -290,10 +307,11 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
 //            and sixteen rows j;
 //   softmax  per lane, in the log2 domain, against a reference m taken from
 //            the head's first tile with a selected row: p = 2^(s - m).  The
-//            accumulator is never rescaled (which keeps it in the accumulation
-//            registers); if a head's probabilities in one tile sum past 2^32
-//            (a later score beat m by about 32), which no realistic attention
-//            does, the head is flagged and the merge recomputes it exactly;
+//            accumulator is never rescaled (which keeps it in the
+//            accumulation registers).  If a lane's probabilities in one tile
+//            sum past 2^64 (a later score beat m by about 60), which no
+//            realistic attention does, the workgroup runs the split again
+//            with each head's largest score as m (kRerunSum);
 //   mix      O~^T[c][h] += sum_j V^T[c][j] P^T[j][h] over all 512 columns c of
 //            the wave's own heads (v_mfma 32x32x16).  The probabilities, packed
 //            to bf16 where the score accumulator left them, already form the
@@ -420,10 +438,15 @@ constexpr int kScDepth = MLA_SC_DEPTH;
 constexpr int kMixDepth = MLA_MIX_DEPTH;
 static_assert(kMixDepth >= 3 && kMixDepth <= 8, "mix read-ahead out of range");
 
-// A head whose per-tile probability sum exceeds this (relative to its
-// reference) is recomputed exactly by the merge; below it, no probability or
-// partial sum comes near the float/bf16 range.
-constexpr float kBeatenSum = 4294967296.f;   // 2^32
+// While no lane's probabilities in one tile sum past this (no scaled score
+// beat its head's reference by more than about 60 in log2 units), no
+// probability, partial sum of at most 2048 of them, or mix of them with
+// latent values comes near the float range; probabilities far below the
+// reference underflow to 0 exactly where they are negligible against the
+// reference's own weight of 1.  A split whose sum does pass it is run again:
+// first a pass that only finds each head's largest score, then the full pass
+// with that as the reference, so that every probability is at most 1.
+constexpr float kRerunSum = 18446744073709551616.f;   // 2^64
 
 // One pass over the split's tiles.  Software pipeline, per iteration t: the
 // score MFMAs of tile t+1 run with the softmax of tile t and the gathers of
@@ -432,11 +455,16 @@ constexpr float kBeatenSum = 4294967296.f;   // 2^32
 // next iteration (own gathers of tile t+2 landed, then a barrier) before its
 // last four MFMAs.
 // The reference of each head is the (scaled) maximum of its first tile with
-// a selected row; no rescaling happens afterwards.  `beaten` reports a tile
-// whose probabilities exceeded kBeatenSum against that reference.
+// a selected row, or, with `preset`, the value m_ref holds on entry.  The
+// accumulator is never rescaled; `beaten` reports a tile whose probabilities
+// passed kRerunSum (the pass's result is then to be discarded).
+// kMaxOnly: the same tile pipeline with no exponentials and no mix; on
+// return m_ref holds each head's largest scaled score over the selected rows.
+template <bool kMaxOnly>
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
-                                          float& l_run, bool& beaten) {
+                                          float& l_run, bool& beaten, bool preset) {
     const int lane = c.lane;
+    beaten = false;
     // A slot is selected iff 0 <= p < lim (p < T and, for prefill, p <= limit).
     const unsigned lim = min((unsigned)c.T, (unsigned)c.limit + 1u);
     // Query fragments (B operands): head 32*wave + lane%32, columns
@@ -475,11 +503,14 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     barrier_lds();
     const int* wave_last = c.sidx + kMaxSlotsPerSplit;
     const int ntiles = (max(max(wave_last[0], wave_last[1]), max(wave_last[2], wave_last[3])) + kRows) / kRows;
+    if constexpr (!kMaxOnly) {
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-    l_run = 0.f;
+        for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
+    }
+    l_run = kMaxOnly ? -INFINITY : 0.f;  // max-only passes keep their running maximum here
     if (ntiles == 0) {                   // nothing selected: an empty partial
         __builtin_amdgcn_s_waitcnt(0);   // no load may land after the workgroup ends
+        if constexpr (kMaxOnly) m_ref = -INFINITY;
         return;
     }
 
@@ -597,7 +628,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // that are not selected (only in partial tiles) and take the reference
     // from the first tile with a selected slot.  Returns the score multiplier
     // to use (1 once masking has applied the scale).
-    bool have_ref = false;
+    bool have_ref = preset;
     // Read once: inside the loop the compiler would reload it from the
     // kernel arguments every tile (the assembly blocks clobber memory), and a
     // scalar load is waited for together with every LDS read in flight.
@@ -620,7 +651,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i] * sc);
-            m_ref = fmaxf(mx, __shfl_xor(mx, 32));   // a head spans lanes l and l ^ 32
+            m_ref = pair_max(mx);                    // a head spans lanes l and l ^ 32
             have_ref = true;
         }
         return sc;
@@ -633,7 +664,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     };
     auto close_sum = [&](float psum) {
         l_run += psum;
-        beaten = beaten || !(psum <= kBeatenSum);
+        beaten = beaten || !(psum <= kRerunSum);
     };
 
     // Mix of the wave's own heads over all 512 latent columns, one tile:
@@ -653,14 +684,18 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
                        lds_read_tr(tiles + (((tr_base[kc][1] + bo) ^ x) + y)));
         };
         bf16x8 va[kMixDepth];
+        if constexpr (!kMaxOnly) {
 #pragma unroll
-        for (int d = 0; d < kMixDepth; ++d) va[d] = v_read(d);
+            for (int d = 0; d < kMixDepth; ++d) va[d] = v_read(d);
+        }
 #pragma unroll
         for (int m = 0; m < 32; ++m) {
-            const bf16x8 av = va[m % kMixDepth];
-            if (m + kMixDepth < 32) va[m % kMixDepth] = v_read(m + kMixDepth);
             if ((m & 3) == 0) before(m >> 2);
-            acc[m & 15] = mfma32(av, pbm[m >> 4], acc[m & 15]);
+            if constexpr (!kMaxOnly) {
+                const bf16x8 av = va[m % kMixDepth];
+                if (m + kMixDepth < 32) va[m % kMixDepth] = v_read(m + kMixDepth);
+                acc[m & 15] = mfma32(av, pbm[m >> 4], acc[m & 15]);
+            }
             if ((m & 3) == 3) after(m >> 2);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -710,6 +745,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     auto body = [&](int t, f32x16& scur, f32x16& snext) {
         const float sc = prepare(t, scur, sel);
         const float neg_m = have_ref ? -m_ref : 0.f;
+        float mx = -INFINITY;            // max-only passes
         const int bo = ((t + 1) & (kBufs - 1)) * kBufBytes;
         const int pidx = gather_index(t + 3);
         bf16x8 pb[2];
@@ -725,12 +761,17 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
             // one exponential every other k-step, so that each fits in the
             // shadow of the MFMA in flight; each k-step is a scheduling
             // region of its own, or the compiler bunches the exponentials
-            if (ks < 32 && !(ks & 1)) prob(scur, ks >> 1, sc, neg_m, pb, psum);
-            if (ks == 32) close_sum(psum);
+            if constexpr (kMaxOnly) {
+                if (ks < 16) mx = fmaxf(mx, scur[ks] * sc);
+            } else {
+                if (ks < 32 && !(ks & 1)) prob(scur, ks >> 1, sc, neg_m, pb, psum);
+            }
             if (ks == 18) issue_rows4(t + 3, 0, goff[0]);
             if (ks == 26) issue_rows4(t + 3, 1, goff[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (kMaxOnly) l_run = fmaxf(l_run, mx);
+        else close_sum(psum);
         mix(t, pb, [&](int idx) {
                    if (idx == 0) read_rows(t + 4);
                    if (idx == 7) hand_over(t + 2);
@@ -746,9 +787,14 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         const float neg_m = have_ref ? -m_ref : 0.f;
         bf16x8 pb[2];
         float psum = 0.f;
+        if constexpr (kMaxOnly) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) prob(scur, i, sc, neg_m, pb, psum);
-        close_sum(psum);
+            for (int i = 0; i < 16; ++i) l_run = fmaxf(l_run, scur[i] * sc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) prob(scur, i, sc, neg_m, pb, psum);
+            close_sum(psum);
+        }
         mix(t, pb, [](int) {}, [](int) {});
     };
 
@@ -782,6 +828,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     }
     last(t, sA);
     MLA_WAIT_VMCNT(0);                   // no gather may land after the workgroup ends
+    if constexpr (kMaxOnly) m_ref = pair_max(l_run);   // a head spans lanes l and l ^ 32
 }
 
 // Write this split's mix in bf16, not normalised (+ reference and sum; the
@@ -790,14 +837,18 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
 // wave holds all 512 columns of its own 32 heads (a head's columns split
 // between lanes l and l ^ 32).  Rows are staged in LDS (the tile buffers are
 // free once every wave is done with them) and every head row is written with
-// one 1 KiB store instruction.
+// one 1 KiB store instruction: stores straight from the accumulator layout
+// would write sixteen scattered 16-byte pieces per instruction, and the
+// memory system's cost goes with the number of pieces.  A wave stages and
+// stores only its own heads' rows, and its LDS accesses run in order, so no
+// barrier separates the two.
 constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (spreads banks)
 
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
-                                            float l_run, bool beaten) {
+                                            float l_run) {
     const AttnArgs& a = *c.a;
     const int lane = c.lane;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);   // a head spans lanes l and l ^ 32
+    const float l_tot = pair_sum(l_run);                 // a head spans lanes l and l ^ 32
     const int h_own = 32 * c.wave + (lane & 31);
     barrier_only();                                      // every wave is done with the tiles
 
@@ -811,7 +862,6 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
             *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
                 to_bf16x4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
         }
-    barrier_lds();
     __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
     const unsigned char* stage = c.tiles + 32 * c.wave * kOutRow;
 #pragma unroll 8
@@ -819,13 +869,10 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOutRow + 16 * lane);
         *reinterpret_cast<u32x4*>(dst0 + (size_t)row * kLatent + 8 * lane) = v;
     }
-    // A head whose probabilities outgrew its reference is marked with a
-    // negative sum; the merge recomputes it exactly.
-    beaten = beaten || __shfl_xor((int)beaten, 32);
     if (lane < 32) {
         const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h_own;
         a.m_part[orow] = m_ref;
-        a.l_part[orow] = beaten ? -1.f : l_tot;
+        a.l_part[orow] = l_tot;
     }
 }
 
@@ -878,8 +925,7 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, co
 // LDS of the attention pass: tile buffers, the split's index list and each
 // wave's last selected slot.
 constexpr int kAttnTilesLds = kBufs * kBufBytes;
-constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4 + 4 * 4;   // + each wave's last selected slot
-static_assert(kHeads * kOutRow <= kAttnTilesLds, "output staging must fit in the tile buffers");
+constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4 + 8 * 4;   // + per wave: last selected slot, rerun flag
 static_assert(kAttnLds <= 160 * 1024, "attention LDS exceeds a compute unit's 160 KiB");
 
 __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* pe, const int32_t* idx,
@@ -893,104 +939,44 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* 
         return;
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
-    bool beaten = false;
-    attn_pass(c, m_ref, acc, l_run, beaten);
-    attn_finish(c, acc, m_ref, l_run, beaten);
+    bool beaten;
+    attn_pass<false>(c, m_ref, acc, l_run, beaten, false);
+    // A split in which a later score beat its head's reference by about 60
+    // (log2 units) runs again, by every wave: a pass that finds each head's
+    // largest score, then the full pass with it as the reference (never the
+    // case for realistic attention; the benchmark times a forced case).
+    int* any_beaten = reinterpret_cast<int*>(lds + kAttnTilesLds) + kMaxSlotsPerSplit + 4;
+    const bool wave_beaten = __builtin_amdgcn_ballot_w64(beaten) != 0;   // every lane takes part
+    if ((threadIdx.x & 63) == 0) any_beaten[c.wave] = wave_beaten;
+    barrier_lds();                       // also: every wave is done with the tiles
+    if (any_beaten[0] | any_beaten[1] | any_beaten[2] | any_beaten[3]) {
+        attn_pass<true>(c, m_ref, acc, l_run, beaten, true);
+        barrier_lds();                   // every wave is done with the tiles
+        attn_pass<false>(c, m_ref, acc, l_run, beaten, true);
+        if (threadIdx.x == 0) atomicAdd(a.stats, 1);
+    }
+    attn_finish(c, acc, m_ref, l_run);
 }
 
 // --------------------------------------------------------------------------
 // Step 4 merge + step 5: out[r, h, :] = O~[r, h, :] . W_UV[h]^T
 //
 // Per head a [R x 512] . [512 x 128] product, computed transposed:
-// out^T = W_UV[h] . O~^T, so W_UV rows (d) are the A operand, loaded straight
-// from HBM with 16-byte reads (c is contiguous in the weight).  Workgroup =
-// (head, group of 32-row query blocks); wave w owns 32 values d and keeps its
-// W_UV slice (32 x 512) in registers.
-// Each 32-row block of O~ is built in LDS: the split partials of up to four
-// splits at a time are loaded straight into LDS (latent chunk c of row j at
-// the same swizzled position as in the attention tiles), merged in float32
-// with weights w_s = 2^(m_s - max) / sum_s' l_s' 2^(m_s' - max) (the partials
-// are not normalised), and written back as bf16 into the first split's rows,
-// which then feed the MFMA B operand.
+// out^T = W_UV[h] . O~^T, with W_UV rows (d) as the A operand in registers.
+// Workgroup = (head, group of 32-row query blocks); wave w owns output values
+// d = 32w .. 32w+31.  Each wave merges eight rows of the block: all of its partial loads are
+// issued at once (loads of every split of a row land while the weights are
+// computed), merged in float32 with w_s = 2^(m_s - M) / sum_s' l_s' 2^(m_s' - M)
+// (M: the largest reference among splits with a selected slot; a split with
+// l_s = 0 weighs 0) and stored to LDS as bf16, swizzled as the attention
+// tiles are; after a barrier every wave multiplies the 32 merged rows.
 // --------------------------------------------------------------------------
 constexpr int kUvRows = 32;
-constexpr int kUvGroup = 4;                    // splits staged in LDS at a time
-constexpr int kUvStage = kUvGroup * kUvRows * 1024;
+constexpr int kUvChunk = 4;                    // splits whose loads are in flight together
+constexpr int kUvLds = kUvRows * 1024;
 
-// LDS byte offset of bf16 column col of staged row j (16-byte chunk swizzle).
-__device__ __forceinline__ int uv_pos(int j, int col) {
-    const int c8 = col >> 3;
-    return j * 1024 + (((c8 & ~15) | ((c8 & 15) ^ lat_swz(j))) << 4) + ((col & 7) << 1);
-}
-
-// Exact mix of one (query row, head) in float32, for a head whose first-tile
-// reference was beaten during the attention pass: pass one finds the maximum
-// score over the row's whole index list, pass two weighs and mixes the
-// selected latent rows (one 256-slot chunk at a time).  The result,
-// normalised, is written to out[0..511].  All 256 threads take part.
-__device__ void exact_mix(const AttnArgs& a, int rr, int h, float* out, float* red, float* p_s,
-                          int* pos_s) {
-    const int tid = threadIdx.x;
-    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q);
-    const __bf16* kv = reinterpret_cast<const __bf16*>(a.kv) + (size_t)rr * a.cache_rows_per_query * kLatent;
-    const __bf16* pe = reinterpret_cast<const __bf16*>(a.pe) + (size_t)rr * a.cache_rows_per_query * kRope;
-    const int32_t* idx = a.idx + (size_t)rr * a.k;
-    const int limit = a.causal_base < 0 ? 0x7fffffff : a.causal_base + rr;
-    auto score = [&](int t) {
-        float d = 0.f;
-        for (int c = 0; c < kLatent; ++c) d += (float)qb[q_off(rr, h, c)] * (float)kv[(size_t)t * kLatent + c];
-        for (int c = 0; c < kRope; ++c)
-            d += (float)qb[q_off(rr, h, kLatent + c)] * (float)pe[(size_t)t * kRope + c];
-        return d * a.scale_log2;
-    };
-    auto block_max = [&](float v) {
-        for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-        __syncthreads();
-        if ((tid & 63) == 0) red[tid >> 6] = v;
-        __syncthreads();
-        return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    };
-    float m = -INFINITY;
-    for (int base = 0; base < a.k; base += 256) {
-        const int slot = base + tid;
-        const int t = slot < a.k ? idx[slot] : -1;
-        if (t >= 0 && t < a.T && t <= limit) m = fmaxf(m, score(t));
-    }
-    m = block_max(m);
-    float acc0 = 0.f, acc1 = 0.f, lp = 0.f;
-    for (int base = 0; base < a.k; base += 256) {
-        const int slot = base + tid;
-        int t = slot < a.k ? idx[slot] : -1;
-        if (!(t >= 0 && t < a.T && t <= limit)) t = -1;
-        const float p = t >= 0 ? exp2f(score(t) - m) : 0.f;
-        lp += p;
-        __syncthreads();
-        p_s[tid] = p;
-        pos_s[tid] = t;
-        __syncthreads();
-        for (int jj = 0; jj < 256; ++jj) {
-            const int tj = pos_s[jj];
-            if (tj < 0) continue;
-            acc0 += p_s[jj] * (float)kv[(size_t)tj * kLatent + tid];
-            acc1 += p_s[jj] * (float)kv[(size_t)tj * kLatent + tid + 256];
-        }
-    }
-    for (int o = 32; o > 0; o >>= 1) lp += __shfl_xor(lp, o);
-    __syncthreads();
-    if ((tid & 63) == 0) red[tid >> 6] = lp;
-    __syncthreads();
-    const float L = red[0] + red[1] + red[2] + red[3];
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    out[tid] = acc0 * inv;
-    out[tid + 256] = acc1 * inv;
-    __syncthreads();
-}
-
-// LDS of one merge + W_UV block: staged partials, then small per-row arrays.
-constexpr int kUvSmall = (2 * kUvRows + kUvGroup * kUvRows + kUvRows + kLatent + 4 + 256 + 256) * 4;
-constexpr int kUvLds = kUvStage + kUvSmall;
-
-// Wave w's slice of W_UV[h] (rows d = 32w .. 32w+31) as MFMA A fragments.
+// Wave w's slice of W_UV[h] (rows d = 32w .. 32w+31) as MFMA A fragments:
+// k-step ks, lane half g takes columns 16ks + 8g .. +7.
 __device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h, bf16x8 (&wa)[32]) {
     const int lane = threadIdx.x & 63;
     const int d = 32 * wave_id() + (lane & 31);
@@ -999,351 +985,142 @@ __device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h
     for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
 }
 
-// The merge kernel's counterpart of AttnEarly: what a workgroup needs before
-// its first loads, passed as leading scalar parameters.
-struct UvEarly {
-    const __bf16* o;
-    const float* m_part;
-    const float* l_part;
-    int R, n_split;
-};
-
-// Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31; `lds` holds kUvLds
-// bytes (1 KiB aligned).  Every thread of the workgroup calls it.
-template <bool kLoadW>
-__device__ __forceinline__ void uv_block(const AttnArgs& a, const UvEarly& e, __bf16* __restrict__ out, int h, int rb,
-                                         bf16x8 (&wa)[32], unsigned char* lds,
-                                         const __bf16* __restrict__ w_uv) {
-    unsigned char* stage = lds;
-    float* s_mmax = reinterpret_cast<float*>(lds + kUvStage);
-    float* s_inv = s_mmax + kUvRows;
-    float (*s_w)[kUvRows] = reinterpret_cast<float (*)[kUvRows]>(s_inv + kUvRows);
-    int* marked = reinterpret_cast<int*>(s_inv + kUvRows + kUvGroup * kUvRows);
-    float* xo = reinterpret_cast<float*>(marked + kUvRows);
-    float* xred = xo + kLatent;
-    float* xp = xred + 4;
-    int* xpos = reinterpret_cast<int*>(xp + 256);
-    const int R = e.R;
-    const int n_split = e.n_split;
-    const int tid = threadIdx.x;
+// Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31.  Every thread of
+// the workgroup calls it; `lds` holds kUvLds bytes (1 KiB aligned).
+__device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const float* __restrict__ m_part,
+                                         const float* __restrict__ l_part, __bf16* __restrict__ out, int R,
+                                         int n_split, int h, int rb, const bf16x8 (&wa)[32],
+                                         unsigned char* lds) {
     const int wave = wave_id();
-    const int lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
-    const unsigned stage_addr = (unsigned)(size_t)stage;
-    const __bf16* o_ws = e.o;
+    const size_t split_stride = (size_t)R * kHeads;           // partial rows between splits
+    const int r0 = rb * kUvRows + 8 * wave;                    // this wave's first row
+    const int nr = max(0, min(8, R - r0));                     // its rows inside R
 
-    // Partial rows (split g0 + wave, query row rb*32 + j) -> staged row
-    // (wave, j); rows past R or splits past n_split load zeros.
-    auto stage_group = [&](int rb, int g0) {
-        const int sp = g0 + wave;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        // rows j of split sp sit kHeads * kLatent bf16 apart in the workspace
-        const bool sp_ok = sp < n_split;
-        const __bf16* src0 = o_ws + (((size_t)(sp_ok ? sp : 0) * R + rb * kUvRows) * kHeads + h) * kLatent;
-        const unsigned row_bytes = kHeads * kLatent * 2;
-        const u32x4 desc = make_desc_x4(src0, sp_ok ? (unsigned)min(R - rb * kUvRows, kUvRows) * row_bytes : 0u);
-#pragma unroll 2
-        for (int j0 = 0; j0 < kUvRows; j0 += 4) {
-            unsigned v[4];
+    // This wave's partial rows of splits s0 .. s0+kUvChunk-1 (zeros past the
+    // last split or past R), 16 bytes per lane and row: columns 8l .. 8l+7.
+    bf16x8 v[kUvChunk][8];
+    auto issue = [&](int s0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = j0 + u;
-                const bool ok = sp_ok && rb * kUvRows + j < R;
-                v[u] = x4_off(ok, (unsigned)j * row_bytes + (unsigned)(((ln & ~15) | ((ln & 15) ^ lat_swz(j))) << 4), u);
+        for (int u = 0; u < kUvChunk; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const bool ok = s0 + u < n_split && jj < nr;
+                const __bf16* src = o_ws + ((size_t)(s0 + u) * split_stride + (size_t)(r0 + jj) * kHeads + h) * kLatent;
+                v[u][jj] = ok ? *reinterpret_cast<const bf16x8*>(src + 8 * lane) : bf16x8{};
             }
-            load_lds16_x4(desc, stage_addr + (wave * kUvRows + j0) * 1024, v[0], v[1], v[2], v[3]);
+    };
+    issue(0);
+
+    // Merge weights, computed while the first partial loads are in flight.
+    // Lane l works on row jj = l / 8 of the wave's eight rows and on the
+    // splits s with s % 8 == l % 8; the eight lanes of a row then combine
+    // their (reference, sum) pairs into the row's largest reference M and
+    // the inverse of its total weight sum_s l_s 2^(m_s - M).
+    const int wj = lane >> 3, wu = lane & 7;
+    const bool wrow = wj < nr;
+    const size_t wrow_off = (size_t)(r0 + (wrow ? wj : 0)) * kHeads + h;
+    float mrow = -INFINITY, lrow = 0.f;
+    for (int sp = wu; sp < n_split; sp += 8) {
+        const float l = wrow ? l_part[sp * split_stride + wrow_off] : 0.f;
+        const float m = wrow ? m_part[sp * split_stride + wrow_off] : -INFINITY;
+        if (l > 0.f) {
+            const float mn = fmaxf(mrow, m);
+            lrow = lrow * exp2f(mrow - mn) + l * exp2f(m - mn);
+            mrow = mn;
         }
-    };
-    // Merge weight of a split with reference m and sum l for a row with
-    // maximum mm and inverse weight sum inv: l 2^(m - mm) inv; a split with no
-    // selected slot (l = 0) or an inexact one (l < 0) weighs 0.
-    // Weight of a split's (unnormalised) partial: 2^(m - mm) / (sum over the
-    // splits of l 2^(m - mm)), with inv that sum's inverse.
-    auto weight = [&](float m, float l, float mm, float inv) {
-        return l > 0.f ? exp2f(m - mm) * inv : 0.f;
-    };
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+        const float m2 = __shfl_xor(mrow, o), l2 = __shfl_xor(lrow, o);
+        const float mn = fmaxf(mrow, m2);
+        lrow = (lrow > 0.f ? lrow * exp2f(mrow - mn) : 0.f) + (l2 > 0.f ? l2 * exp2f(m2 - mn) : 0.f);
+        mrow = mn;
+    }
+    const float inv_row = lrow > 0.f ? 1.f / lrow : 0.f;
 
+    // Merged rows: lane l holds columns 8l .. 8l+7 of each of its rows.
+    float x[8][8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[jj][e] = 0.f;
+    for (int s0 = 0;;) {
+        // weight of split s0 + (l % 8) for row l / 8 (lanes with l % 8 >= kUvChunk idle)
+        float w = 0.f;
+        if (wrow && wu < kUvChunk && s0 + wu < n_split) {
+            const size_t o = (size_t)(s0 + wu) * split_stride + wrow_off;
+            const float l = l_part[o];
+            w = l > 0.f ? exp2f(m_part[o] - mrow) * inv_row : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUvChunk; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float wv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), 8 * jj + u));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[jj][e] = fmaf(wv, (float)v[u][jj][e], x[jj][e]);
+            }
+        s0 += kUvChunk;
+        if (s0 >= n_split) break;
+        issue(s0);
+    }
+    // Stage the merged rows (bf16) for the B operand: 16-byte chunk l of row j
+    // at chunk (l & ~15) | ((l & 15) ^ lat_swz(j)).
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * wave + jj;
+        bf16x8 b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (__bf16)x[jj][e];
+        *reinterpret_cast<bf16x8*>(lds + j * 1024 + (((lane & ~15) | ((lane & 15) ^ lat_swz(j))) << 4)) = b;
+    }
+    barrier_lds();
 
-    // merge lanes: thread -> staged row mj, chunks mp[i] = 8i + (tid % 8), with
-    // the 8-chunk groups of odd rows rotated to spread LDS banks
-    const int mj = tid >> 3;
-    const int msub = tid & 7;
-
-    // out^T[d][r] = sum_c W_UV[d][c] O~[r][c]; B operand column r = lane % 32
+    // out^T[d][r] = sum_c W[d][c] O~[r][c]; B operand column r = lane % 32
     const int j = lane & 31;
     const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
-    auto uv_product = [&](int sl) {
-        f32x16 part = {};
-        const unsigned char* src = stage + sl * kUvRows * 1024;
+    f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(src + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
-            part = mfma32(wa[ks], bv, part);
-        }
-        return part;
-    };
-    auto store_out = [&](const f32x16& acc) {
-        const int r = rb * kUvRows + j;
-        if (r < R) {
-            __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<bf16x4*>(dst + 8 * g) =
-                    to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-        }
-    };
-    // heads whose attention pass was marked inexact: recompute exactly into
-    // staged slot 0 and give those columns its product instead
-    auto exact_heads = [&](f32x16& acc) {
-        int any = 0;
-        for (int row = 0; row < kUvRows; ++row) any |= marked[row];
-        if (!any) return;
-        __syncthreads();                     // every staged row read
-        for (int row = 0; row < kUvRows; ++row) {
-            if (!marked[row]) continue;
-            exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
-            for (int c = tid; c < kLatent; c += 256)
-                *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
-            __syncthreads();
-        }
-        const f32x16 part = uv_product(0);
-        if (marked[j]) acc = part;
-    };
-
-    if (n_split <= kUvGroup) {
-        // Every split fits in LDS at once.  Each wave fetches rows 8w .. 8w+7
-        // of every split with plain 16-byte loads (a run of LDS-direct load
-        // groups would go one group at a time per wave, as each group's M0
-        // must stay put until it lands) and writes them to LDS, two splits
-        // at a time.  Order of the loads: the per-split maxima and sums, the
-        // first two splits, W_UV (on the first block), the other two splits,
-        // so that every wait the compiler places for a register counts only
-        // loads issued after it.  The products run split by split as the
-        // data lands and are combined with the merge weights in float32 (the
-        // product is linear in O~).
-        const int rr_m = rb * kUvRows + mj;
-        const bool have = rr_m < R && msub < n_split;
-        float m0 = -INFINITY, l0 = 0.f;
-        if (have) {
-            const size_t o = ((size_t)msub * R + rr_m) * kHeads + h;
-            l0 = e.l_part[o];
-            m0 = e.m_part[o];
-        }
-        // rows of one split as a buffer (rows past R read zeros, no branch)
-        const unsigned row_bytes = kHeads * kLatent * 2;
-        const int rows_here = min(R - rb * kUvRows, kUvRows);
-        auto load_rows = [&](int sp, u32x4 (&v)[8]) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-                o_ws + (((size_t)sp * R + rb * kUvRows) * kHeads + h) * kLatent, (unsigned)rows_here * row_bytes);
-#pragma unroll
-            for (int r8 = 0; r8 < 8; ++r8)
-                v[r8] = buf_load16(rs, (unsigned)(8 * wave + r8) * row_bytes + 16u * lane);
-        };
-        auto store_rows = [&](int sp, const u32x4 (&v)[8]) {
-#pragma unroll
-            for (int r8 = 0; r8 < 8; ++r8) {
-                const int jj = 8 * wave + r8;
-                *reinterpret_cast<u32x4*>(stage + (sp * kUvRows + jj) * 1024 +
-                                          (((lane & ~15) | ((lane & 15) ^ lat_swz(jj))) << 4)) = v[r8];
-            }
-        };
-        f32x16 part[kUvGroup];
-        {
-            u32x4 v0[8], v1[8];
-            load_rows(0, v0);
-            if (n_split > 1) load_rows(1, v1);
-            if (kLoadW) uv_load_w(w_uv, h, wa);
-            store_rows(0, v0);
-            if (n_split > 1) store_rows(1, v1);
-        }
-        barrier_lds();                       // splits 0 and 1 of every wave in LDS
-        if (n_split > 2) {
-            u32x4 v2[8], v3[8];
-            load_rows(2, v2);
-            if (n_split > 3) load_rows(3, v3);
-            part[0] = uv_product(0);
-            part[1] = uv_product(1);
-            store_rows(2, v2);
-            if (n_split > 3) store_rows(3, v3);
-            barrier_lds();                   // splits 2 and 3 in LDS
-            part[2] = uv_product(2);
-            if (n_split > 3) part[3] = uv_product(3);
-        } else {
-            part[0] = uv_product(0);
-            if (n_split > 1) part[1] = uv_product(1);
-        }
-        // merge weights: lane msub of row mj holds split msub's (m, l)
-        float mloc = -INFINITY, wloc = 0.f;
-        int bad = 0;
-        if (have) {
-            bad = l0 < 0.f;
-            if (l0 > 0.f) {
-                mloc = m0;
-                wloc = l0;
-            }
-        }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            const float m2 = __shfl_xor(mloc, o);
-            const float w2 = __shfl_xor(wloc, o);
-            const float mx = fmaxf(mloc, m2);
-            wloc = (wloc > 0.f ? wloc * exp2f(mloc - mx) : 0.f) + (w2 > 0.f ? w2 * exp2f(m2 - mx) : 0.f);
-            mloc = mx;
-            bad |= __shfl_xor(bad, o);
-        }
-        const float inv = wloc > 0.f ? 1.f / wloc : 0.f;
-        if (msub == 0) marked[mj] = bad;
-        if (msub < kUvGroup) s_w[msub][mj] = (have && !bad) ? weight(m0, l0, mloc, inv) : 0.f;
-        __syncthreads();
-        f32x16 acc = {};
-#pragma unroll
-        for (int sl = 0; sl < kUvGroup; ++sl) {
-            if (sl >= n_split) break;
-            const float w = s_w[sl][j];
-            if (w != 0.f)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] += w * part[sl][i];
-        }
-        exact_heads(acc);
-        store_out(acc);
-        __syncthreads();                     // staging reused by the next block
-        return;
+    for (int ks = 0; ks < 32; ++ks) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lds + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+        acc = mfma32(wa[ks], bv, acc);
     }
-
-    {
-        stage_group(rb, 0);
-        // per-row maximum, inverse weight sum and inexact flag over all splits;
-        // lanes mj*8 .. mj*8+7 share row mj, lane msub takes splits msub + 8i
-        {
-            const int rr = rb * kUvRows + mj;
-            float mloc = -INFINITY, wloc = 0.f, m0 = -INFINITY, l0 = 0.f;
-            int bad = 0;
-            if (rr < R) {
-                for (int sp = msub; sp < n_split; sp += 8) {
-                    const size_t o = ((size_t)sp * R + rr) * kHeads + h;
-                    const float l = e.l_part[o];
-                    const float m = e.m_part[o];
-                    if (sp == msub) {
-                        m0 = m;
-                        l0 = l;
-                    }
-                    bad |= l < 0.f;
-                    const bool ok = l > 0.f;
-                    const float mn = ok ? fmaxf(mloc, m) : mloc;
-                    wloc = (wloc > 0.f ? wloc * exp2f(mloc - mn) : 0.f) + (ok ? l * exp2f(m - mn) : 0.f);
-                    mloc = mn;
-                }
-            }
+    const int r = rb * kUvRows + j;
+    if (r < R) {
+        __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
 #pragma unroll
-            for (int o = 1; o < 8; o <<= 1) {
-                const float m2 = __shfl_xor(mloc, o);
-                const float w2 = __shfl_xor(wloc, o);
-                const float mx = fmaxf(mloc, m2);
-                wloc = (wloc > 0.f ? wloc * exp2f(mloc - mx) : 0.f) + (w2 > 0.f ? w2 * exp2f(m2 - mx) : 0.f);
-                mloc = mx;
-                bad |= __shfl_xor(bad, o);
-            }
-            const float inv = wloc > 0.f ? 1.f / wloc : 0.f;
-            if (msub == 0) {
-                s_mmax[mj] = mloc;
-                s_inv[mj] = inv;
-                marked[mj] = bad;
-            }
-            // weights of the first staged group come from the values at hand; a
-            // head marked for exact recomputation takes nothing from its splits
-            if (msub < kUvGroup)
-                s_w[msub][mj] = (rr < R && msub < n_split && !bad) ? weight(m0, l0, mloc, inv) : 0.f;
-        }
-        float x[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-
-        for (int g0 = 0; g0 < n_split; g0 += kUvGroup) {
-            if (g0 > 0) {
-                __syncthreads();             // previous group fully read
-                stage_group(rb, g0);
-                if (tid < kUvGroup * kUvRows) {
-                    const int sl = tid >> 5, j = tid & 31;
-                    const int rr = rb * kUvRows + j;
-                    float w = 0.f;
-                    if (rr < R && g0 + sl < n_split) {
-                        const size_t o = ((size_t)(g0 + sl) * R + rr) * kHeads + h;
-                        w = weight(e.m_part[o], e.l_part[o], s_mmax[j], s_inv[j]);
-                    }
-                    s_w[sl][j] = w;
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);   // own partial rows landed
-            __syncthreads();                 // all rows and weights visible
-            const int gn = min(kUvGroup, n_split - g0);
-            for (int sl = 0; sl < gn; ++sl) {
-                const float w = s_w[sl][mj];
-                if (w == 0.f) continue;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int pos = (8 * i + msub) ^ ((mj & 1) << 3);
-                    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + (sl * kUvRows + mj) * 1024 + pos * 16);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[i][e] += w * (float)v[e];
-                }
-            }
-        }
-        __syncthreads();                     // every staged row read
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int pos = (8 * i + msub) ^ ((mj & 1) << 3);
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[i][e];
-            *reinterpret_cast<bf16x8*>(stage + mj * 1024 + pos * 16) = v;
-        }
-        __syncthreads();
-        // heads whose attention pass was marked inexact: recompute exactly
-        for (int row = 0; row < kUvRows; ++row) {
-            if (!marked[row]) continue;
-            exact_mix(a, rb * kUvRows + row, h, xo, xred, xp, xpos);
-            for (int c = tid; c < kLatent; c += 256)
-                *reinterpret_cast<__bf16*>(stage + uv_pos(row, c)) = (__bf16)xo[c];
-            __syncthreads();
-        }
-        store_out(uv_product(0));
-        __syncthreads();                     // staging reused by the next block
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<bf16x4*>(dst + 8 * g) = to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
     }
+    barrier_only();                      // staging reused by the next block
 }
 
-__global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* o, const float* m_part, const float* l_part,
+__global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, const float* __restrict__ m_part,
+                                                  const float* __restrict__ l_part,
                                                   const __bf16* __restrict__ w_uv, int R, int n_split,
-                                                  int r_groups, __bf16* __restrict__ out, AttnArgs a) {
+                                                  int r_groups, __bf16* __restrict__ out) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvLds];
-    const UvEarly early{o, m_part, l_part, R, n_split};
     const int h = blockIdx.x;
     bf16x8 wa[32];
-    // With at most kUvGroup splits the first block loads W_UV itself, after
-    // its first partial rows; otherwise W_UV is loaded here, once.
-    int rb = blockIdx.y;
-    if (n_split <= kUvGroup) {
-        uv_block<true>(a, early, out, h, rb, wa, lds, w_uv);
-        rb += r_groups;
-    } else {
-        uv_load_w(w_uv, h, wa);
-    }
-    for (; rb * kUvRows < R; rb += r_groups) uv_block<false>(a, early, out, h, rb, wa, lds, w_uv);
+    uv_load_w(w_uv, h, wa);
+    for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups)
+        uv_block(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
 }
 
 }  // namespace
 
 hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
-                              int R, hipStream_t s) {
+                              int R, int* stats, hipStream_t s) {
     // one workgroup per (head, quarter of c) and eight query blocks: the
     // weight is read once per eight blocks
     const int blocks = (R + 31) / 32;
     const int r_groups = (blocks + 7) / 8;
     hipLaunchKernelGGL(absorb_q_bf16, dim3(kHeads * 4, r_groups), dim3(256), 0, s,
                        static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_pe),
-                       static_cast<const __bf16*>(w_uk), static_cast<__bf16*>(q_out), R, r_groups);
+                       static_cast<const __bf16*>(w_uk), static_cast<__bf16*>(q_out), R, r_groups, stats);
     return hipGetLastError();
 }
 
@@ -1360,7 +1137,7 @@ hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStr
     const int r_groups = blocks < 8 ? blocks : 8;
     hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, static_cast<const __bf16*>(a.o),
                        a.m_part, a.l_part, static_cast<const __bf16*>(w_uv), a.R, a.n_split, r_groups,
-                       static_cast<__bf16*>(out), a);
+                       static_cast<__bf16*>(out));
     return hipGetLastError();
 }
 

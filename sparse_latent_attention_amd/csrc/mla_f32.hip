@@ -11,8 +11,10 @@ namespace {
 __global__ __launch_bounds__(256) void absorb_q_f32(const float* __restrict__ q_nope,
                                                     const float* __restrict__ q_pe,
                                                     const float* __restrict__ w_uk,
-                                                    float* __restrict__ q_out, long long total) {
+                                                    float* __restrict__ q_out, long long total,
+                                                    int* stats) {
     const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e == 0) *stats = 0;   // the call's diagnostics (this path never reruns a split)
     if (e >= total) return;
     const int c = (int)(e % kQRow);
     const long long rh = e / kQRow;
@@ -180,12 +182,12 @@ __global__ __launch_bounds__(256) void validate_idx(const int32_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
-                             int R, hipStream_t s) {
+                             int R, int* stats, hipStream_t s) {
     const long long total = (long long)R * kHeads * kQRow;
     const unsigned blocks = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(absorb_q_f32, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(q_nope),
                        static_cast<const float*>(q_pe), static_cast<const float*>(w_uk),
-                       static_cast<float*>(q_out), total);
+                       static_cast<float*>(q_out), total, stats);
     return hipGetLastError();
 }
 

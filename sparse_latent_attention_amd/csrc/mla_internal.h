@@ -30,6 +30,7 @@ struct Workspace {
     size_t q_off, q_bytes;        // absorbed queries [R, 128, 576] in the call dtype
     size_t o_off, o_bytes;        // mixed latent per split [n_split, R, 128, 512]
     size_t ml_off, ml_bytes;      // per split reference max / probability sum [n_split, R, 128] x2 (f32)
+    size_t stats_off;             // diagnostics of the call: int32 count of rerun splits
     size_t total;
     int n_split;                  // splits of each row's index list
     int slots_per_split;          // index-list slots per split (multiple of kTileRows)
@@ -50,19 +51,22 @@ struct AttnArgs {
     void* o;                // see Workspace::o
     float* m_part;          // [n_split, R, 128]
     float* l_part;          // [n_split, R, 128]
+    int* stats;             // diagnostics (see Workspace::stats_off); zeroed by the absorb kernel
 };
 
 // Launchers (return hipSuccess or the launch error).  The attention launchers
 // take optional start and stop events, which the kernel's dispatch itself
 // timestamps (hipExtLaunchKernel): the interval is the kernel's own duration.
+// The absorb launchers also zero the call's diagnostics (`stats`), which the
+// attention kernel that follows them on the stream then counts into.
 hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
-                              int R, hipStream_t s);
+                              int R, int* stats, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                             hipEvent_t stop = nullptr);
 hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s);
 
 hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
-                             int R, hipStream_t s);
+                             int R, int* stats, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);
 hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,

@@ -51,7 +51,8 @@ Workspace plan_workspace(int rows, int k, int dtype) {
     w.o_bytes = (size_t)n * R * kHeads * kLatent * (bf16 ? 2 : 4);
     w.ml_off = round_up(w.o_off + w.o_bytes, kAlign);
     w.ml_bytes = 2 * (size_t)n * R * kHeads * 4;
-    w.total = round_up(w.ml_off + w.ml_bytes, kAlign);
+    w.stats_off = round_up(w.ml_off + w.ml_bytes, kAlign);
+    w.total = w.stats_off + kAlign;
     return w;
 }
 
@@ -83,12 +84,13 @@ mla_status run(const void* q_nope, const void* q_pe, const void* kv_cache, const
     a.o = ws + w.o_off;
     a.m_part = reinterpret_cast<float*>(ws + w.ml_off);
     a.l_part = reinterpret_cast<float*>(ws + w.ml_off) + (size_t)w.n_split * R * kHeads;
+    a.stats = reinterpret_cast<int*>(ws + w.stats_off);
 
     hipError_t e;
     if (dtype == MLA_BF16)
-        e = launch_absorb_bf16(q_nope, q_pe, w_uk, ws + w.q_off, R, stream);
+        e = launch_absorb_bf16(q_nope, q_pe, w_uk, ws + w.q_off, R, a.stats, stream);
     else
-        e = launch_absorb_f32(q_nope, q_pe, w_uk, ws + w.q_off, R, stream);
+        e = launch_absorb_f32(q_nope, q_pe, w_uk, ws + w.q_off, R, a.stats, stream);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
     hipEvent_t eb = g_attn_begin, ee = g_attn_end;
@@ -127,7 +129,7 @@ const char* mla_status_string(int s) {
     }
 }
 
-int mla_abi_version(void) { return 1; }
+int mla_abi_version(void) { return 2; }
 
 size_t mla_sparse_decode_workspace_size(int B, int T, int k, int dtype) {
     if (!dtype_ok(dtype) || B < 1 || T < 1 || T > kMaxT || k < 1 || k > T) return 0;
@@ -183,6 +185,19 @@ mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int T, int 
     if (!aligned16(idx) || (reinterpret_cast<uintptr_t>(d_flag) & 3u)) return MLA_ERR_ALIGN;
     return launch_validate(idx, rows, k, T, allow_pad, d_flag, stream) == hipSuccess ? MLA_OK
                                                                                        : MLA_ERR_HIP;
+}
+
+mla_status mla_read_rerun_count(const void* workspace, int rows, int k, int dtype, int* d_count,
+                                hipStream_t stream) {
+    if (!workspace || !d_count) return MLA_ERR_NULL;
+    if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+    if (rows < 1 || k < 1) return MLA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(d_count) & 3u) != 0) return MLA_ERR_ALIGN;
+    const Workspace w = plan_workspace(rows, k, dtype);
+    const unsigned char* src = static_cast<const unsigned char*>(workspace) + w.stats_off;
+    return hipMemcpyAsync(d_count, src, sizeof(int), hipMemcpyDeviceToDevice, stream) == hipSuccess
+               ? MLA_OK
+               : MLA_ERR_HIP;
 }
 
 mla_status mla_set_attention_events(hipEvent_t begin, hipEvent_t end) {

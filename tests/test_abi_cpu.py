@@ -46,17 +46,17 @@ def test_status_strings(lib):
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(code).decode().startswith(name)
     assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
 
 
 def ws_expected(rows, esize, n_split):
-    """Absorbed queries, per-split mixes (bf16 or f32), per-split max and sum."""
+    """Absorbed queries, per-split mixes (bf16 or f32), per-split max and sum, diagnostics."""
     def up(x):
         return (x + 255) // 256 * 256
     q = rows * 128 * 576 * esize
     o = n_split * rows * 128 * 512 * esize
     ml = 2 * n_split * rows * 128 * 4
-    return up(up(up(q) + o) + ml)
+    return up(up(up(q) + o) + ml) + 256          # + the call's diagnostics
 
 
 def test_cache_length_limit(lib):
@@ -151,6 +151,11 @@ def test_validator_and_event_hook_argument_checks(lib):
     assert lib.mla_validate_indices(MISALIGNED, 1, 1, 1, 0, FAKE, None) == 3
     assert lib.mla_set_attention_events(FAKE, None) == 1
     assert lib.mla_set_attention_events(None, None) == 0
+    assert lib.mla_read_rerun_count(None, 1, 1, 1, FAKE, None) == 1
+    assert lib.mla_read_rerun_count(FAKE, 1, 1, 1, None, None) == 1
+    assert lib.mla_read_rerun_count(FAKE, 1, 1, 5, FAKE, None) == 4
+    assert lib.mla_read_rerun_count(FAKE, 0, 1, 1, FAKE, None) == 2
+    assert lib.mla_read_rerun_count(FAKE, 1, 1, 1, ctypes.c_void_p(0x10002), None) == 3
 
 
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):

@@ -1,9 +1,11 @@
 """GPU parity: the HIP library against the fp64 CPU oracle.
 
 Tolerance (per tensor): max|gpu - oracle| / max|oracle| <= 1e-5 for float32
-inputs and <= 2e-2 for bf16 inputs.  Small configurations are compared on
-every output; full-size configurations on sampled query rows, in the same
-launch configuration the benchmark times.
+inputs and <= 2e-2 for bf16 inputs.  Decode configurations are compared on
+every batch row, the headline one in the launch configuration the benchmark
+times; the 4096-query prefill chunk on a strided sample that reaches every
+workgroup slot, both sides of the 2048-position list limit and the last 64
+queries.
 """
 import numpy as np
 import pytest
@@ -70,12 +72,35 @@ def test_config1_page_shape_dense(mla):
     check_decode(mla, synth.CONFIGS["page_dense_bf16"])
 
 
-def test_config2_sparse_b32(mla):
-    check_decode(mla, synth.CONFIGS["sparse_b32_t8k"], rows=[0, 1, 7, 16, 30, 31])
+def test_config2_sparse_b32_all_rows(mla):
+    check_decode(mla, synth.CONFIGS["sparse_b32_t8k"])
 
 
-def test_config3_headline_sampled(mla):
-    check_decode(mla, synth.CONFIGS["sparse_b64_t32k"], rows=[0, 21, 42, 63])
+def test_config3_headline_all_rows(mla):
+    out, inp, dev = check_decode(mla, synth.CONFIGS["sparse_b64_t32k"])
+    # unit-variance logits never beat a split's first-tile reference by ~60 (log2)
+    assert rerun_count(mla, dev, inp) == 0
+
+
+def _prefill_rows(S):
+    """Every 16th query, offset so that the sample meets every residue mod 8 (the attention
+    kernel deals query rows to workgroups, and workgroups to XCDs, by those residues), plus
+    both sides of the query whose list first fills all 2048 slots, and the last 64 queries."""
+    strided = [16 * i + (i % 8) for i in range(S // 16)]
+    return sorted(set(strided) | set(range(2040, 2056)) | set(range(S - 64, S)))
+
+
+def _oracle_prefill_parallel(inp, rows, start_pos, workers=8):
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = [rows[i::workers] for i in range(workers)]
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda rr: oracle.prefill(inp, rows=rr, start_pos=start_pos), chunks))
+    ref = np.empty((len(rows), 128, 128))
+    pos = {r: i for i, r in enumerate(rows)}
+    for rr, part in zip(chunks, parts):
+        for r, o in zip(rr, part):
+            ref[pos[r]] = o
+    return ref
 
 
 def test_config4_prefill_sampled(mla):
@@ -85,11 +110,13 @@ def test_config4_prefill_sampled(mla):
     assert np.array_equal(dev["topk_idx"].cpu().numpy(), inp["topk_idx"])
     log(f"prefill {cfg.name}: S={cfg.S} T={cfg.T} k={cfg.k}")
     out = to_host64(run_prefill(mla, dev, cfg.start_pos))
-    rows = [0, 1, 2, 63, 64, 1000, 2046, 2047, 2048, 3333, 4095]
-    ref = oracle.prefill(inp, rows=rows, start_pos=cfg.start_pos)
+    assert np.all(np.isfinite(out))
+    rows = _prefill_rows(cfg.S)
+    assert len(rows) >= 256 and {r % 8 for r in rows} == set(range(8))
+    ref = _oracle_prefill_parallel(inp, rows, cfg.start_pos)
     err = rel_err(out[rows], ref)
-    log(f"  rows {rows}: rel err {err:.3e}")
-    assert np.all(np.isfinite(out)) and err <= TOL["bf16"]
+    log(f"  {len(rows)} queries: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 # ------------------------------------------------------------------ ragged and small
@@ -131,7 +158,7 @@ def _bf16_decode_workspace(rows, k, n_split):
     q = rows * 128 * 576 * 2
     o = n_split * rows * 128 * 512 * 2
     ml = 2 * n_split * rows * 128 * 4
-    return up(up(up(q) + o) + ml)
+    return up(up(up(q) + o) + ml) + 256          # + the call's diagnostics
 
 
 @pytest.mark.parametrize("B,k,n_split", [(64, 32, 1), (64, 64, 2), (64, 96, 3), (64, 128, 4),
@@ -250,6 +277,25 @@ def test_validate_indices(mla):
     assert mla.validate_indices(to_dev(inp["topk_idx"]), T=8192) == 0
 
 
+def test_side_stream_with_int64_indices(mla):
+    # A call on a side stream, with int64 indices the binding converts: the conversion,
+    # the workspace and the output are made on that stream after it has waited for the
+    # current one, so the result equals the same call on the current stream.
+    cfg = DecodeConfig(24, "side_stream", B=3, T=900, k=200, dtype="bf16")
+    inp = synth.decode_inputs(cfg)
+    dev = upload(inp)
+    ref = run_decode(mla, dev).clone()
+    side = torch.cuda.Stream()
+    q_nope = dev["q_nope"] * 1.0            # produced on the current stream just before the call
+    idx64 = dev["topk_idx"].to(torch.int64)
+    out = mla.decode(q_nope, dev["q_pe"], dev["kv_cache"], dev["pe_cache"], idx64, dev["w_uk"],
+                     dev["w_uv"], stream=side)
+    assert mla.validate_indices(idx64, T=cfg.T, stream=side) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 def test_attention_event_hook(mla):
     cfg = DecodeConfig(20, "ev", B=4, T=1000, k=256, dtype="bf16")
     dev = upload(synth.decode_inputs(cfg))
@@ -264,20 +310,110 @@ def test_attention_event_hook(mla):
     assert 0.0 < ms < 1000.0
 
 
-def test_large_logits_take_the_exact_path(mla):
-    # With W_UK = 0 the scores are scale * (q_pe . k_R), computed from exact bf16
-    # inputs, so a large scale spreads them over tens of log2 units without
-    # amplifying any rounding.  Later tiles then beat the first tile's reference
-    # by more than 2^32 for many heads, and the merge recomputes those exactly.
-    cfg = DecodeConfig(21, "big_logits", B=64, T=2000, k=1024, dtype="bf16")
+def _split_plan(rows, k):
+    """(splits, slots per split) of the attention work split: about 256 workgroups, whole
+    32-slot tiles, at most 2048 slots per split; confirmed against the workspace size the
+    library reports for that many splits."""
+    n = -(-256 // rows)
+    n = max(min(n, -(-k // 32)), -(-k // 2048), 1)
+    per = -(-(-(-k // n)) // 32) * 32
+    n = -(-k // per)
+    assert _MLA["m"].decode_workspace_size(rows, k, k, torch.bfloat16) == _bf16_decode_workspace(rows, k, n)
+    return n, per
+
+
+_MLA = {}
+
+
+def predicted_excess(inp, scale, rows, k, causal_base=None):
+    """Largest amount (log2 units) by which a scaled score beats its split's reference, the
+    maximum of the split's first 32-slot tile that holds a selected position, over every
+    (query, split, head); computed in float64 from the inputs (the scores' definition).
+    causal_base: prefill queries see positions <= causal_base + query."""
+    n, per = _split_plan(rows, k)
+    qc = np.einsum("rhd,hdc->rhc", oracle.to_f64(inp["q_nope"]), oracle.to_f64(inp["w_uk"]))
+    worst = -np.inf
+    for r in range(rows):
+        kv = inp["kv_cache"][r] if causal_base is None else inp["kv_cache"]
+        pe = inp["pe_cache"][r] if causal_base is None else inp["pe_cache"]
+        T = kv.shape[0]
+        lim = T - 1 if causal_base is None else min(T - 1, causal_base + r)
+        idx = inp["topk_idx"][r]
+        for sp in range(n):
+            slots = idx[sp * per:(sp + 1) * per]
+            ok = (slots >= 0) & (slots <= lim)
+            if not ok.any():
+                continue
+            pos = np.where(ok, slots, 0)
+            sc = (qc[r] @ oracle.to_f64(kv[pos]).T + oracle.to_f64(inp["q_pe"][r]) @ oracle.to_f64(pe[pos]).T)
+            sc = np.where(ok[None, :], sc * scale * np.log2(np.e), -np.inf)      # [128, slots]
+            tiles = [sc[:, i:i + 32] for i in range(0, sc.shape[1], 32)]
+            first = next(t for t in tiles if np.isfinite(t).any())
+            ref = first.max(axis=1)
+            worst = max(worst, float(np.max(sc.max(axis=1) - ref)))
+    return worst
+
+
+def rerun_count(mla, dev, inp, scale=None, prefill_start=None):
+    """Run the call again with a workspace the test holds and read its rerun count."""
+    rows = dev["q_nope"].shape[0]
+    k = dev["topk_idx"].shape[1]
+    if prefill_start is None:
+        ws = torch.empty(mla.decode_workspace_size(rows, dev["kv_cache"].shape[1], k, torch.bfloat16),
+                         dtype=torch.uint8, device="cuda:0")
+        kw = {} if scale is None else {"softmax_scale": scale}
+        run_decode(mla, dev, workspace=ws, **kw)
+    else:
+        ws = torch.empty(mla.prefill_chunk_workspace_size(rows, dev["kv_cache"].shape[0], k,
+                                                          torch.bfloat16),
+                         dtype=torch.uint8, device="cuda:0")
+        run_prefill(mla, dev, prefill_start, workspace=ws, softmax_scale=scale)
+    return mla.rerun_count(ws, rows, k, torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,T,k", [(64, 2000, 1024), (8, 3000, 2048)])
+def test_large_logits_rerun_the_split(mla, B, T, k):
+    # With W_UK = 0 the scores are scale * (q_pe . k_R), computed from exact bf16 inputs,
+    # so a large scale spreads them over hundreds of log2 units without amplifying any
+    # rounding.  Later tiles then beat their split's first-tile reference by far more
+    # than 60 (log2), and those splits run again with each head's largest score as the
+    # reference.  64 rows give four splits of eight tiles; 8 rows give 32 splits of two
+    # tiles, which the merge takes four at a time.
+    _MLA["m"] = mla
+    cfg = DecodeConfig(21, "big_logits", B=B, T=T, k=k, dtype="bf16")
     inp = synth.decode_inputs(cfg)
     inp["w_uk"] = np.zeros_like(inp["w_uk"])
-    scale = 3.0
-    out = to_host64(run_decode(mla, upload(inp), softmax_scale=scale))
-    rows = [0, 17, 40, 63]
-    ref = oracle.decode(inp, rows=rows, scale=scale)
-    err = rel_err(out[rows], ref)
-    log(f"large logits: rel err {err:.3e}")
+    scale = 10.0
+    excess = predicted_excess(inp, scale, B, k)
+    log(f"large logits B={B}: largest excess over a split reference {excess:.1f} (log2)")
+    assert excess > 90                       # far past the rerun threshold
+    dev = upload(inp)
+    out = to_host64(run_decode(mla, dev, softmax_scale=scale))
+    n = rerun_count(mla, dev, inp, scale=scale)
+    log(f"  splits rerun: {n}")
+    assert n > 0
+    ref = oracle.decode(inp, scale=scale)
+    err = rel_err(out, ref)
+    log(f"  all rows: rel err {err:.3e}")
+    assert np.all(np.isfinite(out)) and err <= TOL["bf16"]
+
+
+def test_large_logits_rerun_causal_prefill(mla):
+    # The same forced case in a causal prefill chunk: 256 queries take one split each
+    # (128 slots, four tiles), and each stops at its own position.
+    _MLA["m"] = mla
+    cfg = PrefillConfig(23, "prefill_big_logits", S=256, T=600, k=128, start_pos=300, dtype="bf16")
+    inp = synth.prefill_inputs(cfg)
+    inp["w_uk"] = np.zeros_like(inp["w_uk"])
+    scale = 10.0
+    excess = predicted_excess(inp, scale, cfg.S, cfg.k, causal_base=cfg.start_pos)
+    log(f"prefill large logits: largest excess {excess:.1f} (log2)")
+    assert excess > 90
+    dev = upload(inp)
+    out = to_host64(run_prefill(mla, dev, cfg.start_pos, softmax_scale=scale))
+    assert rerun_count(mla, dev, inp, scale=scale, prefill_start=cfg.start_pos) > 0
+    err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos, scale=scale))
+    log(f"  all queries: rel err {err:.3e}")
     assert np.all(np.isfinite(out)) and err <= TOL["bf16"]
 
 
