@@ -108,6 +108,32 @@ MLA_API mla_status mla_sparse_decode(const void* q_nope, const void* q_pe,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, arguments, checks and errors as
+ * mla_sparse_decode, with the workspace taken from a fixed array of
+ * MLA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on, from the first such call until the process ends.  The call itself
+ * allocates nothing.
+ *
+ * Returns MLA_ERR_WORKSPACE when mla_sparse_decode_workspace_size(B, T, k,
+ * dtype) exceeds MLA_NOALLOC_SCRATCH_BYTES (B = 64, k = 2048 in bf16 needs
+ * 41.3 MiB and fits; large k at small B, or float32, may not).  Every call on
+ * one device shares that device's array, which keeps the last call's
+ * contents: calls that overlap on one device (different streams, or threads
+ * without ordering) race and corrupt each other's results; calls queued on
+ * one stream are ordered and safe.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (48 * 1024 * 1024)
+
+MLA_API mla_status mla_sparse_decode_noalloc(const void* q_nope, const void* q_pe,
+                                             const void* kv_cache, const void* pe_cache,
+                                             const int32_t* topk_idx,
+                                             const void* w_uk, const void* w_uv, void* out,
+                                             int B, int T, int ld_T, int k, float softmax_scale,
+                                             int dtype, hipStream_t stream);
+
+/*
  * Prefill chunk in latent form: S consecutive queries of ONE sequence against
  * its cache.  Query s sits at absolute position start_pos + s and ignores any
  * listed position greater than that (the causal mask the model adds in its

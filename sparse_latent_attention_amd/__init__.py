@@ -16,8 +16,9 @@ from ._lib import MLA_BF16, MLA_F32, MLAError  # noqa: F401
 
 N_HEADS, D_LATENT, D_ROPE, D_NOPE, D_V = 128, 512, 64, 128, 128
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
+NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "prefill_chunk", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "rerun_count", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -148,6 +149,37 @@ def decode(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, T=None,
                                    float(softmax_scale), code, _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream))
         _lib.check(st, "mla_sparse_decode")
+        return out
+
+
+def decode_noalloc(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, out, T=None,
+                   softmax_scale=SOFTMAX_SCALE, stream=None):
+    """Decode into the caller's ``out`` through the library's allocation-free entry point.
+
+    The library takes the workspace from a fixed device array of its own
+    (MLA_NOALLOC_SCRATCH_BYTES); calls that overlap on one device race.  The
+    binding itself only allocates when it has to convert int64 indices.
+    """
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = q_nope.dtype, q_nope.device
+        B = q_nope.shape[0]
+        ld_T = kv_cache.shape[1]
+        T = ld_T if T is None else int(T)
+        idx = _index32(topk_idx)
+        k = idx.shape[1]
+        _require(q_nope, "q_nope", (B, N_HEADS, D_NOPE), dt, dev)
+        _require(q_pe, "q_pe", (B, N_HEADS, D_ROPE), dt, dev)
+        _require(kv_cache, "kv_cache", (B, ld_T, D_LATENT), dt, dev)
+        _require(pe_cache, "pe_cache", (B, ld_T, D_ROPE), dt, dev)
+        _require(idx, "topk_idx", (B, k), torch.int32, dev)
+        _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
+        _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
+        _require(out, "out", (B, N_HEADS, D_V), dt, dev)
+        st = lib.mla_sparse_decode_noalloc(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
+                                           _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), B, T, ld_T,
+                                           k, float(softmax_scale), _dtype_code(dt), _stream(stream))
+        _lib.check(st, "mla_sparse_decode_noalloc")
         return out
 
 

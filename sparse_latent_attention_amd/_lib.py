@@ -25,6 +25,8 @@ SIGNATURES = {
     "mla_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "mla_sparse_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                _I, _I, _I, _I, _F, _I, _VP, _SZ, _VP]),
+    "mla_sparse_decode_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       _I, _I, _I, _I, _F, _I, _VP]),
     "mla_sparse_prefill_chunk_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "mla_sparse_prefill_chunk": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _I, _I, _I, _I, _F, _I, _VP, _SZ, _VP]),

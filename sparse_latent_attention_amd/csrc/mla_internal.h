@@ -38,6 +38,13 @@ struct Workspace {
 
 Workspace plan_workspace(int rows, int k, int dtype);
 
+// Host-side argument checks of mla_sparse_decode (everything but the
+// workspace); returns MLA_OK (0) or the error code, touching no device.
+int check_decode_args(const void* q_nope, const void* q_pe, const void* kv_cache,
+                      const void* pe_cache, const int32_t* topk_idx, const void* w_uk,
+                      const void* w_uv, const void* out, int B, int T, int ld_T, int k,
+                      float softmax_scale, int dtype);
+
 struct AttnArgs {
     const void* q;          // [R, 128, 576] absorbed queries
     const void* kv;         // latent cache base

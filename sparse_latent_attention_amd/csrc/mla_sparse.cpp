@@ -109,6 +109,23 @@ mla_status run(const void* q_nope, const void* q_pe, const void* kv_cache, const
 bool dtype_ok(int dtype) { return dtype == MLA_F32 || dtype == MLA_BF16; }
 
 }  // namespace
+
+int check_decode_args(const void* q_nope, const void* q_pe, const void* kv_cache,
+                      const void* pe_cache, const int32_t* topk_idx, const void* w_uk,
+                      const void* w_uv, const void* out, int B, int T, int ld_T, int k,
+                      float softmax_scale, int dtype) {
+    if (!q_nope || !q_pe || !kv_cache || !pe_cache || !topk_idx || !w_uk || !w_uv || !out)
+        return MLA_ERR_NULL;
+    if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+    if (B < 1 || T < 1 || T > kMaxT || k < 1 || k > T || ld_T < T) return MLA_ERR_SHAPE;
+    if (dtype == MLA_F32 && B > 65535) return MLA_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+        !aligned16(topk_idx) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
+        return MLA_ERR_ALIGN;
+    return MLA_OK;
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -146,15 +163,9 @@ mla_status mla_sparse_decode(const void* q_nope, const void* q_pe, const void* k
                              const void* w_uv, void* out, int B, int T, int ld_T, int k,
                              float softmax_scale, int dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-    if (!q_nope || !q_pe || !kv_cache || !pe_cache || !topk_idx || !w_uk || !w_uv || !out)
-        return MLA_ERR_NULL;
-    if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
-    if (B < 1 || T < 1 || T > kMaxT || k < 1 || k > T || ld_T < T) return MLA_ERR_SHAPE;
-    if (dtype == MLA_F32 && B > 65535) return MLA_ERR_SHAPE;
-    if (!std::isfinite(softmax_scale)) return MLA_ERR_SHAPE;
-    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
-        !aligned16(topk_idx) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
-        return MLA_ERR_ALIGN;
+    const int st = check_decode_args(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, out, B,
+                                     T, ld_T, k, softmax_scale, dtype);
+    if (st != MLA_OK) return static_cast<mla_status>(st);
     return run(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, out, B, T, ld_T, k, -1,
                softmax_scale, dtype, workspace, workspace_bytes, stream);
 }

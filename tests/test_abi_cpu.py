@@ -158,6 +158,34 @@ def test_validator_and_event_hook_argument_checks(lib):
     assert lib.mla_read_rerun_count(FAKE, 1, 1, 1, ctypes.c_void_p(0x10002), None) == 3
 
 
+def call_noalloc(lib, **kw):
+    args = dict(q_nope=FAKE, q_pe=FAKE, kv=FAKE, pe=FAKE, idx=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE,
+                B=2, T=100, ld_T=100, k=10, scale=0.07, dtype=1, stream=None)
+    args.update(kw)
+    return lib.mla_sparse_decode_noalloc(args["q_nope"], args["q_pe"], args["kv"], args["pe"],
+                                         args["idx"], args["w_uk"], args["w_uv"], args["out"],
+                                         args["B"], args["T"], args["ld_T"], args["k"],
+                                         args["scale"], args["dtype"], args["stream"])
+
+
+def test_noalloc_checks_come_before_any_device_call(lib):
+    hdr = open(HDR).read()
+    cap = eval(re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(([^)]*)\)", hdr).group(1))
+    from sparse_latent_attention_amd import NOALLOC_SCRATCH_BYTES
+    assert cap == NOALLOC_SCRATCH_BYTES == 48 * 2 ** 20
+    for field in ["q_nope", "kv", "idx", "w_uv", "out"]:
+        assert call_noalloc(lib, **{field: None}) == 1
+        assert call_noalloc(lib, **{field: MISALIGNED}) == 3
+    assert call_noalloc(lib, B=0) == 2
+    assert call_noalloc(lib, k=101) == 2
+    assert call_noalloc(lib, dtype=3) == 4
+    # the headline decode fits the fixed scratch; calls whose workspace does not are refused
+    assert lib.mla_sparse_decode_workspace_size(64, 32768, 2048, 1) <= cap
+    assert lib.mla_sparse_decode_workspace_size(128, 32768, 2048, 1) > cap
+    assert call_noalloc(lib, B=128, T=32768, ld_T=32768, k=2048) == 5
+    assert call_noalloc(lib, B=64, T=32768, ld_T=32768, k=2048, dtype=0) == 5
+
+
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
