@@ -165,21 +165,25 @@ MLA_API mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int
 /*
  * Diagnostics of the last decode or prefill call that used `workspace`, with
  * the same row count (B or S), k and dtype: copies, asynchronously on
- * `stream`, the number of index-list splits that call's attention kernel ran
- * a second time into *d_count (device int, caller-owned, 4-byte aligned).
+ * `stream`, two ints into d_out[0..1] (device memory, caller-owned, 4-byte
+ * aligned):
  *
- * The softmax ("Mix and project" page, All 4 steps: A = softmax, O~ = A c^KV)
- * is computed per split of an index list against a reference score per head,
- * taken from the split's first tile of 32 positions with a selected one.
- * When a later score beats that reference by about 60 in log2 units (so that
- * the probabilities could leave the float range), the bf16 path discards the
- * split's pass and runs it again: once to find each head's largest score,
- * then in full with that as the reference.  Each rerun split counts one.
- * The float32 path keeps a running maximum instead and reports 0.
- * Off the hot path; the next call does not read it.
+ *   d_out[0]  index-list splits the attention kernel ran a second time.  The
+ *             softmax ("Mix and project" page, All 4 steps: A = softmax,
+ *             O~ = A c^KV) is computed per split of an index list against a
+ *             reference score per head, taken from the split's first tile of
+ *             32 positions with a selected one.  When a later score beats it
+ *             by about 60 in log2 units (so that the probabilities could leave
+ *             the float range), the bf16 path discards the split's pass and
+ *             runs it again: once to find each head's largest score, then in
+ *             full with that as the reference.  The float32 path keeps a
+ *             running maximum instead and reports 0.
+ *   d_out[1]  reserved; always 0.
+ *
+ * Off the hot path; the next call does not read them.
  */
-MLA_API mla_status mla_read_rerun_count(const void* workspace, int rows, int k, int dtype,
-                                        int* d_count, hipStream_t stream);
+MLA_API mla_status mla_read_diagnostics(const void* workspace, int rows, int k, int dtype,
+                                        int* d_out, hipStream_t stream);
 
 /*
  * Timing hook.  When `begin` and `end` are non-NULL (events the caller has

@@ -19,7 +19,7 @@ SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
 __all__ = ["decode", "decode_noalloc", "prefill_chunk", "decode_workspace_size", "prefill_chunk_workspace_size",
-           "validate_indices", "rerun_count", "set_attention_events", "status_string",
+           "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
 
@@ -232,15 +232,17 @@ def validate_indices(topk_idx, T: int, allow_pad: bool = False, stream=None) -> 
         return int(flag.item())
 
 
-def rerun_count(workspace, rows: int, k: int, dtype: torch.dtype, stream=None) -> int:
-    """Index-list splits the last call that used ``workspace`` ran twice (softmax reference beaten)."""
+def diagnostics(workspace, rows: int, k: int, dtype: torch.dtype, stream=None) -> dict:
+    """Diagnostics of the last call that used ``workspace``: index-list splits it ran twice
+    (softmax reference beaten); the second word is reserved and always 0."""
     with _on_stream(stream):
         lib = _lib.load()
-        cnt = torch.empty(1, dtype=torch.int32, device=workspace.device)
-        st = lib.mla_read_rerun_count(_ptr(workspace), int(rows), int(k), _dtype_code(dtype),
-                                      _ptr(cnt), _stream(stream))
-        _lib.check(st, "mla_read_rerun_count")
-        return int(cnt.item())
+        buf = torch.empty(2, dtype=torch.int32, device=workspace.device)
+        st = lib.mla_read_diagnostics(_ptr(workspace), int(rows), int(k), _dtype_code(dtype),
+                                      _ptr(buf), _stream(stream))
+        _lib.check(st, "mla_read_diagnostics")
+        v = buf.cpu().tolist()
+        return {"reruns": int(v[0]), "reserved": int(v[1])}
 
 
 def set_attention_events(begin, end) -> None:

@@ -31,7 +31,7 @@ SIGNATURES = {
     "mla_sparse_prefill_chunk": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _I, _I, _I, _I, _F, _I, _VP, _SZ, _VP]),
     "mla_validate_indices": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
-    "mla_read_rerun_count": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "mla_read_diagnostics": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "mla_set_attention_events": (_I, [_VP, _VP]),
 }
 

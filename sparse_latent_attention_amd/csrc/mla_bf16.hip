@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
                                                      __bf16* __restrict__ q_out, int R,
                                                      int r_groups, int* stats) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kAbsorbLds];
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *stats = 0;   // the call's diagnostics
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) stats[threadIdx.x] = 0;   // the call's diagnostics
     // Workgroups are dealt to the eight XCDs in turn (id % 8).  XCD x takes
     // heads 16x .. 16x+15 with all four column quarters, so a head's queries
     // come from memory once per launch (the other quarters hit that XCD's L2)

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(256) void absorb_q_f32(const float* __restrict__ q_
                                                     float* __restrict__ q_out, long long total,
                                                     int* stats) {
     const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e == 0) *stats = 0;   // the call's diagnostics (this path never reruns a split)
+    if (e < 2) stats[e] = 0;  // the call's diagnostics (this path never reruns a split)
     if (e >= total) return;
     const int c = (int)(e % kQRow);
     const long long rh = e / kQRow;

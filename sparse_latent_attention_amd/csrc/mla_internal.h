@@ -30,7 +30,7 @@ struct Workspace {
     size_t q_off, q_bytes;        // absorbed queries [R, 128, 576] in the call dtype
     size_t o_off, o_bytes;        // mixed latent per split [n_split, R, 128, 512]
     size_t ml_off, ml_bytes;      // per split reference max / probability sum [n_split, R, 128] x2 (f32)
-    size_t stats_off;             // diagnostics of the call: int32 count of rerun splits
+    size_t stats_off;             // diagnostics of the call: int32 [0] rerun splits, [1] reserved (0)
     size_t total;
     int n_split;                  // splits of each row's index list
     int slots_per_split;          // index-list slots per split (multiple of kTileRows)
@@ -58,7 +58,7 @@ struct AttnArgs {
     void* o;                // see Workspace::o
     float* m_part;          // [n_split, R, 128]
     float* l_part;          // [n_split, R, 128]
-    int* stats;             // diagnostics (see Workspace::stats_off); zeroed by the absorb kernel
+    int* stats;             // diagnostics (see Workspace::stats_off), zeroed before the attention kernel
 };
 
 // Launchers (return hipSuccess or the launch error).  The attention launchers
@@ -71,6 +71,7 @@ hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                             hipEvent_t stop = nullptr);
 hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s);
+
 
 hipError_t launch_absorb_f32(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
                              int R, int* stats, hipStream_t s);

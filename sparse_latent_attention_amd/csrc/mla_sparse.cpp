@@ -198,15 +198,15 @@ mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int T, int 
                                                                                        : MLA_ERR_HIP;
 }
 
-mla_status mla_read_rerun_count(const void* workspace, int rows, int k, int dtype, int* d_count,
+mla_status mla_read_diagnostics(const void* workspace, int rows, int k, int dtype, int* d_out,
                                 hipStream_t stream) {
-    if (!workspace || !d_count) return MLA_ERR_NULL;
+    if (!workspace || !d_out) return MLA_ERR_NULL;
     if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
     if (rows < 1 || k < 1) return MLA_ERR_SHAPE;
-    if ((reinterpret_cast<uintptr_t>(d_count) & 3u) != 0) return MLA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(d_out) & 3u) != 0) return MLA_ERR_ALIGN;
     const Workspace w = plan_workspace(rows, k, dtype);
     const unsigned char* src = static_cast<const unsigned char*>(workspace) + w.stats_off;
-    return hipMemcpyAsync(d_count, src, sizeof(int), hipMemcpyDeviceToDevice, stream) == hipSuccess
+    return hipMemcpyAsync(d_out, src, 2 * sizeof(int), hipMemcpyDeviceToDevice, stream) == hipSuccess
                ? MLA_OK
                : MLA_ERR_HIP;
 }

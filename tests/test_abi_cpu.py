@@ -151,11 +151,11 @@ def test_validator_and_event_hook_argument_checks(lib):
     assert lib.mla_validate_indices(MISALIGNED, 1, 1, 1, 0, FAKE, None) == 3
     assert lib.mla_set_attention_events(FAKE, None) == 1
     assert lib.mla_set_attention_events(None, None) == 0
-    assert lib.mla_read_rerun_count(None, 1, 1, 1, FAKE, None) == 1
-    assert lib.mla_read_rerun_count(FAKE, 1, 1, 1, None, None) == 1
-    assert lib.mla_read_rerun_count(FAKE, 1, 1, 5, FAKE, None) == 4
-    assert lib.mla_read_rerun_count(FAKE, 0, 1, 1, FAKE, None) == 2
-    assert lib.mla_read_rerun_count(FAKE, 1, 1, 1, ctypes.c_void_p(0x10002), None) == 3
+    assert lib.mla_read_diagnostics(None, 1, 1, 1, FAKE, None) == 1
+    assert lib.mla_read_diagnostics(FAKE, 1, 1, 1, None, None) == 1
+    assert lib.mla_read_diagnostics(FAKE, 1, 1, 5, FAKE, None) == 4
+    assert lib.mla_read_diagnostics(FAKE, 0, 1, 1, FAKE, None) == 2
+    assert lib.mla_read_diagnostics(FAKE, 1, 1, 1, ctypes.c_void_p(0x10002), None) == 3
 
 
 def call_noalloc(lib, **kw):

@@ -368,7 +368,9 @@ def rerun_count(mla, dev, inp, scale=None, prefill_start=None):
                                                           torch.bfloat16),
                          dtype=torch.uint8, device="cuda:0")
         run_prefill(mla, dev, prefill_start, workspace=ws, softmax_scale=scale)
-    return mla.rerun_count(ws, rows, k, torch.bfloat16)
+    d = mla.diagnostics(ws, rows, k, torch.bfloat16)
+    assert d["reserved"] == 0
+    return d["reruns"]
 
 
 @pytest.mark.parametrize("B,T,k", [(64, 2000, 1024), (8, 3000, 2048)])
