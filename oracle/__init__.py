@@ -19,6 +19,7 @@ from .mla_oracle import (  # noqa: F401
     absorbed_scores,
     attend_explicit,
     attend_explicit_gather,
+    cache_append,
     decode,
     decode_absorbed,
     explicit_scores,
@@ -27,6 +28,8 @@ from .mla_oracle import (  # noqa: F401
     join_query,
     mix_values,
     prefill,
+    rms_norm,
+    rotate_pairs,
     scores,
     selected_rows,
     softmax_rows,

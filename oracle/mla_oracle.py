@@ -303,3 +303,56 @@ def explicit_scores(q_nope, q_pe, latent, rope, w_uk, w_uv, scale=SOFTMAX_SCALE)
     k_nope, _ = up_project(to_f64(latent), wkv_b)
     keys = join_keys(k_nope, to_f64(rope))
     return scores(join_query(to_f64(q_nope), to_f64(q_pe)), keys, scale)
+
+
+# --------------------------------------------------------------------------
+# cache append: the step that produces the cached latent and rotary key
+# --------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * weight.
+
+    The latent RMSNorm ("KV compression" page, Parameters: 512 learned gains;
+    code: kv = self.kv_norm(kv)).  The pages do not show its epsilon; it is a
+    caller-supplied reading.
+    """
+    x = to_f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * to_f64(weight)
+
+
+def rotate_pairs(x: np.ndarray, cos_sin: np.ndarray) -> np.ndarray:
+    """Interleaved rotary embedding of the last axis.
+
+    Feature pairs (x[2i], x[2i+1]) are the real and imaginary parts of one
+    complex number, which is multiplied by cos(theta_i) + j sin(theta_i)
+    ("Rotated shared key" page, the rotary function with its default
+    interleaved layout, as the key path calls it).  ``cos_sin`` [..., D/2, 2]
+    holds (cos theta_i, sin theta_i) and broadcasts against x's leading axes.
+    """
+    x = to_f64(x)
+    re, im = x[..., 0::2], x[..., 1::2]
+    c, s = to_f64(cos_sin)[..., 0], to_f64(cos_sin)[..., 1]
+    out = np.empty_like(x)
+    out[..., 0::2] = re * c - im * s
+    out[..., 1::2] = re * s + im * c
+    return out
+
+
+def cache_append(kv_a_out, norm_weight, cos_sin, kv_cache, pe_cache, start_pos: int, eps: float):
+    """New cache contents after appending S positions of B sequences.
+
+    kv_a_out [B, S, 576]: the joint down-projection's output, latent (512)
+    then rotary key (64), split after the product ("KV compression" page,
+    Explanation).  The latent is RMS-normalised with the gains norm_weight
+    [512]; the rotary key is rotated with cos_sin [S, 32, 2] (the angles of
+    positions start_pos .. start_pos+S-1).  Both are written to rows
+    start_pos .. start_pos+S-1 of kv_cache [B, T, 512] and pe_cache [B, T, 64]
+    (the model caches these 576 values per position); every other row keeps
+    its value.  Returns (kv_cache, pe_cache) as float64 copies.
+    """
+    a = to_f64(kv_a_out)
+    S = a.shape[1]
+    kv = to_f64(kv_cache).copy()
+    pe = to_f64(pe_cache).copy()
+    kv[:, start_pos:start_pos + S] = rms_norm(a[..., :D_LATENT], norm_weight, eps)
+    pe[:, start_pos:start_pos + S] = rotate_pairs(a[..., D_LATENT:], to_f64(cos_sin)[None])
+    return kv, pe
