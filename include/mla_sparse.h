@@ -153,6 +153,37 @@ MLA_API mla_status mla_sparse_prefill_chunk(const void* q_nope, const void* q_pe
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Cache append: the step that fills the caches the attention reads
+ * ("KV compression" page, Explanation and code: one joint down-projection
+ * gives the 512-wide latent and the 64-wide rotary key, split after the
+ * product; the latent goes through its RMSNorm; the rotary key is rotated;
+ * the model caches these 576 values per position.  "Rotated shared key"
+ * page: the rotary function, with interleaved feature pairs as the key path
+ * calls it).  For each of B sequences and S new positions:
+ *
+ *   c   = kv_a_out[b, s, 0:512] / sqrt(mean(kv_a_out[b, s, 0:512]^2) + eps) * norm_weight
+ *   kR  = kv_a_out[b, s, 512:576] with pair i (features 2i, 2i+1) taken as
+ *         re + j im and multiplied by cos_sin[s, i, 0] + j cos_sin[s, i, 1]
+ *   kv_cache[b, start_pos + s] = c,  pe_cache[b, start_pos + s] = kR
+ *
+ *   kv_a_out    [B, S, 576]    the down-projection's output, in `dtype`
+ *   norm_weight [512]          the latent RMSNorm's gains, in `dtype`
+ *   cos_sin     [S, 32, 2]     float32: cos and sin of the rotary angle of each
+ *                              pair at each new position (the caller's
+ *                              frequency table, sliced to those positions)
+ *   kv_cache    [B, ld_T, 512], pe_cache [B, ld_T, 64], in `dtype`: rows
+ *               start_pos .. start_pos+S-1 are written, no other row is touched
+ *   eps         the RMSNorm epsilon (>= 0; the pages do not give its value)
+ *
+ * Arithmetic in float32, results rounded to `dtype`.  Errors: MLA_ERR_NULL,
+ * MLA_ERR_SHAPE (B or S < 1, start_pos < 0, start_pos + S > ld_T, eps < 0 or
+ * not finite), MLA_ERR_ALIGN, MLA_ERR_DTYPE, MLA_ERR_HIP.
+ */
+MLA_API mla_status mla_cache_append(const void* kv_a_out, const void* norm_weight, const float* cos_sin,
+                                    void* kv_cache, void* pe_cache, int B, int S, int start_pos, int ld_T,
+                                    float eps, int dtype, hipStream_t stream);
+
+/*
  * Debug check of index lists (off the hot path).  For each of `rows` lists of
  * width k: every entry must be in [0, T), or < 0 when allow_pad != 0, and the
  * non-negative entries of a list must be distinct.  Writes into *d_flag

@@ -18,7 +18,7 @@ N_HEADS, D_LATENT, D_ROPE, D_NOPE, D_V = 128, 512, 64, 128, 128
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "decode_noalloc", "prefill_chunk", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "cache_append", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -218,6 +218,32 @@ def prefill_chunk(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, sta
                                           ws.numel() * ws.element_size(), _stream(stream))
         _lib.check(st, "mla_sparse_prefill_chunk")
         return out
+
+
+def cache_append(kv_a_out, norm_weight, cos_sin, kv_cache, pe_cache, *, start_pos, eps=1e-6,
+                 stream=None):
+    """Write S new positions of B sequences into the caches, in place.
+
+    kv_a_out [B, S, 576] (latent then rotary key), norm_weight [512], cos_sin
+    [S, 32, 2] float32, kv_cache [B, ld_T, 512], pe_cache [B, ld_T, 64]; rows
+    start_pos .. start_pos+S-1 receive the RMS-normalised latent and the rotated
+    rotary key.  Returns (kv_cache, pe_cache).
+    """
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = kv_a_out.dtype, kv_a_out.device
+        B, S = kv_a_out.shape[0], kv_a_out.shape[1]
+        ld_T = kv_cache.shape[1]
+        _require(kv_a_out, "kv_a_out", (B, S, D_LATENT + D_ROPE), dt, dev)
+        _require(norm_weight, "norm_weight", (D_LATENT,), dt, dev)
+        _require(cos_sin, "cos_sin", (S, D_ROPE // 2, 2), torch.float32, dev)
+        _require(kv_cache, "kv_cache", (B, ld_T, D_LATENT), dt, dev)
+        _require(pe_cache, "pe_cache", (B, ld_T, D_ROPE), dt, dev)
+        st = lib.mla_cache_append(_ptr(kv_a_out), _ptr(norm_weight), _ptr(cos_sin), _ptr(kv_cache),
+                                  _ptr(pe_cache), B, S, int(start_pos), ld_T, float(eps),
+                                  _dtype_code(dt), _stream(stream))
+        _lib.check(st, "mla_cache_append")
+        return kv_cache, pe_cache
 
 
 def validate_indices(topk_idx, T: int, allow_pad: bool = False, stream=None) -> int:

@@ -80,6 +80,11 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start = 
 hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,
                          const void* w_uv, void* out, int R, int n_split, hipStream_t s);
 
+// Cache append (mla_cache_append): one wave per new position.
+hipError_t launch_cache_append(const void* kv_a_out, const void* norm_weight, const float* cos_sin, void* kv_cache,
+                               void* pe_cache, int B, int S, int start_pos, int ld_T, float eps, bool bf16,
+                               hipStream_t s);
+
 hipError_t launch_validate(const int32_t* idx, int rows, int k, int T, int allow_pad, int* flag,
                            hipStream_t s);
 

@@ -198,6 +198,22 @@ mla_status mla_validate_indices(const int32_t* idx, int rows, int k, int T, int 
                                                                                        : MLA_ERR_HIP;
 }
 
+mla_status mla_cache_append(const void* kv_a_out, const void* norm_weight, const float* cos_sin, void* kv_cache,
+                            void* pe_cache, int B, int S, int start_pos, int ld_T, float eps, int dtype,
+                            hipStream_t stream) {
+    if (!kv_a_out || !norm_weight || !cos_sin || !kv_cache || !pe_cache) return MLA_ERR_NULL;
+    if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+    if (B < 1 || S < 1 || start_pos < 0 || ld_T < 1 || (long long)start_pos + S > ld_T) return MLA_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.f) return MLA_ERR_SHAPE;
+    if (!aligned16(kv_a_out) || !aligned16(norm_weight) || !aligned16(cos_sin) || !aligned16(kv_cache) ||
+        !aligned16(pe_cache))
+        return MLA_ERR_ALIGN;
+    return launch_cache_append(kv_a_out, norm_weight, cos_sin, kv_cache, pe_cache, B, S, start_pos, ld_T, eps,
+                               dtype == MLA_BF16, stream) == hipSuccess
+               ? MLA_OK
+               : MLA_ERR_HIP;
+}
+
 mla_status mla_read_diagnostics(const void* workspace, int rows, int k, int dtype, int* d_out,
                                 hipStream_t stream) {
     if (!workspace || !d_out) return MLA_ERR_NULL;

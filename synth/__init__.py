@@ -5,6 +5,9 @@ attention arithmetic, so both the CPU oracle and the HIP path can consume its
 output without sharing any of the method's code.
 """
 from .generators import (  # noqa: F401
+    AppendConfig,
+    append_inputs,
+    rotary_angles,
     CONFIGS,
     DEFAULT_SEED,
     DecodeConfig,

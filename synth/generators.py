@@ -207,3 +207,41 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = DEFAULT_SEED):
     w_uk, w_uv = weights(cfg, seed)
     return {"q_nope": q_nope, "q_pe": q_pe, "kv_cache": kv, "pe_cache": pe,
             "topk_idx": idx, "w_uk": w_uk, "w_uv": w_uv}
+
+
+@dataclass(frozen=True)
+class AppendConfig:
+    cid: int
+    name: str
+    B: int
+    S: int
+    T: int
+    start_pos: int
+    dtype: str
+
+
+def rotary_angles(positions, dim: int = D_ROPE, base: float = 10000.0) -> np.ndarray:
+    """Rotary table [len(positions), dim/2, 2] float32: (cos, sin) of t * base^(-2i/dim).
+
+    The base frequencies follow the model's table ("Rotated shared key" page,
+    the precomputation's first line); the page leaves out the long-context
+    interpolation and the base value, so this input uses base 10000 and no
+    interpolation.  The library takes the table as given.
+    """
+    freqs = 1.0 / (base ** (np.arange(0, dim, 2, dtype=np.float64) / dim))
+    theta = np.outer(np.asarray(positions, dtype=np.float64), freqs)
+    return np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
+
+
+def append_inputs(cfg: AppendConfig, seed: int = DEFAULT_SEED):
+    """Inputs of a cache append: down-projection output [B, S, 576] (N(0, 1)), latent gains [512]
+    (N(1, 0.1^2)), the rotary table of positions start_pos .. start_pos+S-1, and existing caches
+    [B, T, 512] and [B, T, 64] (N(0, 1)) whose other rows must survive."""
+    rng = np.random.default_rng([seed, cfg.cid, _TAG_CACHE, 7])
+    a = rng.standard_normal((cfg.B, cfg.S, D_LATENT + D_ROPE), dtype=np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(D_LATENT)).astype(np.float32)
+    kv = rng.standard_normal((cfg.B, cfg.T, D_LATENT), dtype=np.float32)
+    pe = rng.standard_normal((cfg.B, cfg.T, D_ROPE), dtype=np.float32)
+    return {"kv_a_out": _store(a, cfg.dtype), "norm_weight": _store(w, cfg.dtype),
+            "cos_sin": rotary_angles(np.arange(cfg.start_pos, cfg.start_pos + cfg.S)),
+            "kv_cache": _store(kv, cfg.dtype), "pe_cache": _store(pe, cfg.dtype)}

@@ -186,6 +186,23 @@ def test_noalloc_checks_come_before_any_device_call(lib):
     assert call_noalloc(lib, B=64, T=32768, ld_T=32768, k=2048, dtype=0) == 5
 
 
+def test_cache_append_argument_checks(lib):
+    def call(**kw):
+        args = dict(a=FAKE, w=FAKE, cs=FAKE, kv=FAKE, pe=FAKE, B=2, S=3, start=5, ld_T=10, eps=1e-6,
+                    dtype=1, stream=None)
+        args.update(kw)
+        return lib.mla_cache_append(args["a"], args["w"], args["cs"], args["kv"], args["pe"], args["B"],
+                                    args["S"], args["start"], args["ld_T"], args["eps"], args["dtype"],
+                                    args["stream"])
+    for field in ["a", "w", "cs", "kv", "pe"]:
+        assert call(**{field: None}) == 1
+        assert call(**{field: MISALIGNED}) == 3
+    for kw in [dict(B=0), dict(S=0), dict(start=-1), dict(start=8), dict(eps=-1.0),
+               dict(eps=float("nan"))]:
+        assert call(**kw) == 2, kw
+    assert call(dtype=2) == 4
+
+
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
