@@ -10,6 +10,7 @@ independent of this code; none is "parity unpinned".
 """
 from .mla_oracle import (  # noqa: F401
     D_LATENT,
+    D_MODEL,
     D_NOPE,
     D_QK,
     D_ROPE,
@@ -27,6 +28,7 @@ from .mla_oracle import (  # noqa: F401
     join_keys,
     join_query,
     mix_values,
+    output_projection,
     prefill,
     rms_norm,
     rotate_pairs,

@@ -356,3 +356,22 @@ def cache_append(kv_a_out, norm_weight, cos_sin, kv_cache, pe_cache, start_pos: 
     kv[:, start_pos:start_pos + S] = rms_norm(a[..., :D_LATENT], norm_weight, eps)
     pe[:, start_pos:start_pos + S] = rotate_pairs(a[..., D_LATENT:], to_f64(cos_sin)[None])
     return kv, pe
+
+
+# --------------------------------------------------------------------------
+# output projection: the step after the path
+# --------------------------------------------------------------------------
+D_MODEL = 7168       # model width
+
+
+def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Delta = o W_O: the 128 heads' outputs joined and projected to the model width.
+
+    ``o`` [B, 128, 128] is the per-head output O_i; it is flattened head by
+    head into [B, 16384] (o = reshape(O), "Mix and project" page, All 4
+    steps; the code flattens the head and value axes).  ``w_o`` is stored as
+    the model's linear layer stores it, [7168 out, 16384 in], so the product
+    is o . w_o^T -> [B, 7168].
+    """
+    o = to_f64(o)
+    return o.reshape(o.shape[0], N_HEADS * D_V) @ to_f64(w_o).T
