@@ -63,6 +63,8 @@ def parse():
                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "this script with --copy-calibration-mib into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     p.add_argument("--traffic-command", default="", help="command line recorded with --write-traffic")
+    p.add_argument("--project", action="store_true",
+                   help="time the output projection at B=64 instead of decode; prints its own JSON line")
     p.add_argument("--prefill", action="store_true",
                    help="time the prefill chunk (S=T=4096, k=min(t+1, 2048), bf16) instead of decode; "
                         "prints its own JSON line (not the headline metric)")
@@ -289,6 +291,40 @@ def bench_prefill(args, torch, synth, mla):
                      "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None}}), flush=True)
 
 
+def bench_project(args, torch, synth, mla):
+    """The output projection Delta = o W_O at the decode batch (B=64): a weight-streaming product
+    whose algorithmic bytes are the 235 MB bf16 weight plus the head outputs and the result."""
+    dev = torch.device("cuda:0")
+    B = 64
+    inp = synth.projection_inputs(B, "bf16")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    o, w = up(inp["o"]), up(inp["w_o"])
+    out = torch.empty((B, 7168), dtype=torch.bfloat16, device=dev)
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    for _ in range(warm):
+        mla.output_projection(o, w, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mla.output_projection(o, w, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = 7168 * 16384 * 2 + B * 16384 * 2 + B * 7168 * 2
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "output projection weight-stream rate (B=64, 7168 x 16384 bf16)", "value": gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic projection_inputs",
+        "config": {"workload": "output projection o [64, 16384] . W_O [7168, 16384]^T, bf16", "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -311,6 +347,9 @@ def main():
     mla._lib.load()
     if args.prefill:
         bench_prefill(args, torch, synth, mla)
+        return
+    if args.project:
+        bench_project(args, torch, synth, mla)
         return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS["sparse_b64_t32k"]

@@ -153,6 +153,27 @@ MLA_API mla_status mla_sparse_prefill_chunk(const void* q_nope, const void* q_pe
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Output projection, the step after the attention ("Mix and project" page,
+ * All 4 steps: o = reshape(O), Delta = o W_O; Parameters: 16,384 x 7,168;
+ * code: the head outputs flattened and passed through the output linear
+ * layer, the only step that mixes heads):
+ *
+ *   out[b, n] = sum_k o[b, k] * w_o[n, k],  k = 128 * head + value
+ *
+ *   o    [B, 128, 128]  per-head outputs (what mla_sparse_decode writes)
+ *   w_o  [7168, 16384]  the output layer's weight in its [out, in] storage
+ *   out  [B, 7168]      written, never read
+ *
+ * bf16: MFMA with float32 accumulation, result rounded to bf16; float32:
+ * float32 throughout.  Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (B < 1),
+ * MLA_ERR_ALIGN, MLA_ERR_DTYPE, MLA_ERR_HIP.
+ */
+#define MLA_D_MODEL 7168
+
+MLA_API mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype,
+                                         hipStream_t stream);
+
+/*
  * Cache append: the step that fills the caches the attention reads
  * ("KV compression" page, Explanation and code: one joint down-projection
  * gives the 512-wide latent and the 64-wide rotary key, split after the

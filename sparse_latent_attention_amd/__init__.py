@@ -15,10 +15,11 @@ from . import _lib
 from ._lib import MLA_BF16, MLA_F32, MLAError  # noqa: F401
 
 N_HEADS, D_LATENT, D_ROPE, D_NOPE, D_V = 128, 512, 64, 128, 128
+D_MODEL = 7168
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "decode_noalloc", "prefill_chunk", "cache_append", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -217,6 +218,22 @@ def prefill_chunk(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, sta
                                           int(start_pos), float(softmax_scale), code, _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream))
         _lib.check(st, "mla_sparse_prefill_chunk")
+        return out
+
+
+def output_projection(o, w_o, *, out=None, stream=None):
+    """Delta = o W_O: o [B, 128, 128] (per-head outputs), w_o [7168, 16384]; returns out [B, 7168]."""
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = o.dtype, o.device
+        B = o.shape[0]
+        _require(o, "o", (B, N_HEADS, D_V), dt, dev)
+        _require(w_o, "w_o", (D_MODEL, N_HEADS * D_V), dt, dev)
+        if out is None:
+            out = torch.empty((B, D_MODEL), dtype=dt, device=dev)
+        _require(out, "out", (B, D_MODEL), dt, dev)
+        st = lib.mla_output_projection(_ptr(o), _ptr(w_o), _ptr(out), B, _dtype_code(dt), _stream(stream))
+        _lib.check(st, "mla_output_projection")
         return out
 
 

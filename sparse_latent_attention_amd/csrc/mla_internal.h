@@ -80,6 +80,11 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start = 
 hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,
                          const void* w_uv, void* out, int R, int n_split, hipStream_t s);
 
+// Output projection (mla_output_projection): [B, 16384] . [7168, 16384]^T.
+constexpr int kProjIn = kHeads * kValue;   // 16,384 joined head outputs
+constexpr int kProjOut = 7168;             // model width
+hipError_t launch_project(const void* o, const void* w_o, void* out, int B, bool bf16, hipStream_t s);
+
 // Cache append (mla_cache_append): one wave per new position.
 hipError_t launch_cache_append(const void* kv_a_out, const void* norm_weight, const float* cos_sin, void* kv_cache,
                                void* pe_cache, int B, int S, int start_pos, int ld_T, float eps, bool bf16,

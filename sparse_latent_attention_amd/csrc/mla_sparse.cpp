@@ -214,6 +214,14 @@ mla_status mla_cache_append(const void* kv_a_out, const void* norm_weight, const
                : MLA_ERR_HIP;
 }
 
+mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype, hipStream_t stream) {
+    if (!o || !w_o || !out) return MLA_ERR_NULL;
+    if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+    if (B < 1 || (long long)B * kProjOut > 0x7fffffffLL) return MLA_ERR_SHAPE;
+    if (!aligned16(o) || !aligned16(w_o) || !aligned16(out)) return MLA_ERR_ALIGN;
+    return launch_project(o, w_o, out, B, dtype == MLA_BF16, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_read_diagnostics(const void* workspace, int rows, int k, int dtype, int* d_out,
                                 hipStream_t stream) {
     if (!workspace || !d_out) return MLA_ERR_NULL;

@@ -18,5 +18,6 @@ from .generators import (  # noqa: F401
     decode_query_set,
     prefill_inputs,
     prefill_query_rows,
+    projection_inputs,
     weights,
 )

@@ -245,3 +245,15 @@ def append_inputs(cfg: AppendConfig, seed: int = DEFAULT_SEED):
     return {"kv_a_out": _store(a, cfg.dtype), "norm_weight": _store(w, cfg.dtype),
             "cos_sin": rotary_angles(np.arange(cfg.start_pos, cfg.start_pos + cfg.S)),
             "kv_cache": _store(kv, cfg.dtype), "pe_cache": _store(pe, cfg.dtype)}
+
+
+D_MODEL = 7168
+
+
+def projection_inputs(B: int, dtype: str, cid: int = 70, seed: int = DEFAULT_SEED):
+    """Per-head outputs o [B, 128, 128] (N(0, 1)) and an output weight w_o [7168, 16384]
+    (N(0, variance 1/16384), so that outputs have unit variance)."""
+    rng = np.random.default_rng([seed, cid, _TAG_WEIGHTS, 2])
+    o = rng.standard_normal((B, N_HEADS, D_V), dtype=np.float32)
+    w = rng.standard_normal((D_MODEL, N_HEADS * D_V), dtype=np.float32) * np.float32(1.0 / 128.0)
+    return {"o": _store(o, dtype), "w_o": _store(w, dtype)}

@@ -203,6 +203,16 @@ def test_cache_append_argument_checks(lib):
     assert call(dtype=2) == 4
 
 
+def test_output_projection_argument_checks(lib):
+    assert lib.mla_output_projection(None, FAKE, FAKE, 2, 1, None) == 1
+    assert lib.mla_output_projection(FAKE, FAKE, None, 2, 1, None) == 1
+    assert lib.mla_output_projection(FAKE, MISALIGNED, FAKE, 2, 1, None) == 3
+    assert lib.mla_output_projection(FAKE, FAKE, FAKE, 0, 1, None) == 2
+    assert lib.mla_output_projection(FAKE, FAKE, FAKE, 2, 9, None) == 4
+    hdr = open(HDR).read()
+    assert int(re.search(r"#define MLA_D_MODEL (\d+)", hdr).group(1)) == 7168
+
+
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
