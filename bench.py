@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="time the prefill chunk (S=T=4096, k=min(t+1, 2048), bf16) instead of decode; "
                         "prints its own JSON line (not the headline metric)")
+    p.add_argument("--prefill-explicit", action="store_true",
+                   help="time the same prefill chunk in the explicit form (keys and values "
+                        "up-projected per head); prints its own JSON line")
     return p.parse_args()
 
 
@@ -242,10 +245,15 @@ def cpu_baseline(cfg, rows_wanted: int):
     return base, extra
 
 
-def bench_prefill(args, torch, synth, mla):
+EXPLICIT_PAIR_FLOPS = 2 * 128 * (192 + 128)   # explicit form: scores + mix for 128 heads
+
+
+def bench_prefill(args, torch, synth, mla, explicit=False):
     """One prefill chunk of one sequence: S = T = 4096 queries from position 0, query t
-    selecting min(t + 1, 2048) positions up to its own.  Throughput is the algorithmic FLOP of
-    the chunk (absorptions plus 278,528 FLOP per selected (query, position) pair) per second."""
+    selecting min(t + 1, 2048) positions up to its own.  Throughput is the chunk's algorithmic
+    FLOP per second.  Latent form: the absorptions plus 278,528 FLOP per selected (query,
+    position) pair.  Explicit form: the up-projection of every visible position's keys and
+    values (2 x 256 x 512 x 128 FLOP each) plus 81,920 FLOP per selected pair."""
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS["prefill_s4096"]
     inp = synth.prefill_inputs(cfg)
@@ -259,16 +267,24 @@ def bench_prefill(args, torch, synth, mla):
     d = {name: up(v) for name, v in inp.items()}
     S, k = cfg.S, cfg.k
     pairs = int((d["topk_idx"] >= 0).sum().item())
-    flop = pairs * ROW_FLOPS + 2 * 2 * S * 128 * 128 * 512
+    if explicit:
+        visible = min(cfg.start_pos + S, cfg.T)
+        flop = pairs * EXPLICIT_PAIR_FLOPS + 2 * visible * 128 * 256 * 512
+        ws = torch.empty(mla.prefill_explicit_workspace_size(S, cfg.T, k, cfg.start_pos, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        entry, form = mla.prefill_explicit, "explicit"
+    else:
+        flop = pairs * ROW_FLOPS + 2 * 2 * S * 128 * 128 * 512
+        ws = torch.empty(mla.prefill_chunk_workspace_size(S, cfg.T, k, torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+        entry, form = mla.prefill_chunk, "latent"
     out = torch.empty((S, 128, 128), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(mla.prefill_chunk_workspace_size(S, cfg.T, k, torch.bfloat16), dtype=torch.uint8,
-                     device=dev)
     steps = min(args.steps, 50)
     warm = min(args.warmup, 10)
 
     def call():
-        mla.prefill_chunk(d["q_nope"], d["q_pe"], d["kv_cache"], d["pe_cache"], d["topk_idx"],
-                          d["w_uk"], d["w_uv"], start_pos=cfg.start_pos, out=out, workspace=ws)
+        entry(d["q_nope"], d["q_pe"], d["kv_cache"], d["pe_cache"], d["topk_idx"],
+              d["w_uk"], d["w_uv"], start_pos=cfg.start_pos, out=out, workspace=ws)
 
     for _ in range(warm):
         call()
@@ -282,10 +298,10 @@ def bench_prefill(args, torch, synth, mla):
     sec = e0.elapsed_time(e1) / 1e3 / steps
     tflops = flop / sec / 1e12
     print(json.dumps({
-        "metric": "prefill chunk FLOP/s (S=T=4096, k=min(t+1,2048))", "value": flop / sec,
+        "metric": f"prefill chunk FLOP/s, {form} form (S=T=4096, k=min(t+1,2048))", "value": flop / sec,
         "unit": "FLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic prefill_s4096 inputs",
-        "config": {"workload": "prefill chunk S=4096, T=4096, k=min(t+1, 2048), 128 heads, bf16",
+        "config": {"workload": f"prefill chunk ({form} form) S=4096, T=4096, k=min(t+1, 2048), 128 heads, bf16",
                    "pairs": pairs, "flop": flop},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None}}), flush=True)
@@ -345,8 +361,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     mla._lib.load()
-    if args.prefill:
-        bench_prefill(args, torch, synth, mla)
+    if args.prefill or args.prefill_explicit:
+        bench_prefill(args, torch, synth, mla, explicit=args.prefill_explicit)
         return
     if args.project:
         bench_project(args, torch, synth, mla)

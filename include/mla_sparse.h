@@ -205,6 +205,33 @@ MLA_API mla_status mla_cache_append(const void* kv_a_out, const void* norm_weigh
                                     float eps, int dtype, hipStream_t stream);
 
 /*
+ * Prefill chunk in the explicit form the pages print for prefill ("Key heads"
+ * page, Explanation: the prefill-branch code: the latent is up-projected into
+ * per-head content keys and values, each head's key joins its content part
+ * with the shared rotary key, scores are scaled, masked by the index list and
+ * the causal mask, normalised and used to mix the values).  Same arguments,
+ * layouts, readings and result as mla_sparse_prefill_chunk (which computes
+ * the absorbed form); bf16 only (MLA_ERR_DTYPE otherwise).
+ *
+ * Computation: the keys and values of positions 0 .. min(start_pos + S, T) - 1
+ * are up-projected into the workspace ([positions, 128, 256] bf16), the index
+ * lists become a bitmap of selected positions per query, and blocks of 128
+ * queries attend, head by head, over every position up to their last query's,
+ * with unselected positions masked.  The workspace must hold
+ * mla_sparse_prefill_explicit_workspace_size(S, T, k, start_pos, dtype) bytes
+ * (0 for invalid arguments or a dtype other than MLA_BF16).
+ */
+MLA_API size_t mla_sparse_prefill_explicit_workspace_size(int S, int T, int k, int start_pos, int dtype);
+
+MLA_API mla_status mla_sparse_prefill_explicit(const void* q_nope, const void* q_pe,
+                                               const void* kv_cache, const void* pe_cache,
+                                               const int32_t* topk_idx,
+                                               const void* w_uk, const void* w_uv, void* out,
+                                               int S, int T, int k, int start_pos, float softmax_scale,
+                                               int dtype, void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
+
+/*
  * Debug check of index lists (off the hot path).  For each of `rows` lists of
  * width k: every entry must be in [0, T), or < 0 when allow_pad != 0, and the
  * non-negative entries of a list must be distinct.  Writes into *d_flag

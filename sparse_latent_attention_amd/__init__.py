@@ -19,7 +19,7 @@ D_MODEL = 7168
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "decode_noalloc", "prefill_chunk", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "prefill_explicit", "prefill_explicit_workspace_size", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -261,6 +261,43 @@ def cache_append(kv_a_out, norm_weight, cos_sin, kv_cache, pe_cache, *, start_po
                                   _dtype_code(dt), _stream(stream))
         _lib.check(st, "mla_cache_append")
         return kv_cache, pe_cache
+
+
+def prefill_explicit_workspace_size(S: int, T: int, k: int, start_pos: int, dtype=torch.bfloat16) -> int:
+    return _lib.load().mla_sparse_prefill_explicit_workspace_size(S, T, k, start_pos, _dtype_code(dtype))
+
+
+def prefill_explicit(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, start_pos=0,
+                     softmax_scale=SOFTMAX_SCALE, out=None, workspace=None, stream=None):
+    """Explicit-form prefill of S queries (bf16): same arguments and result as prefill_chunk."""
+    with _on_stream(stream):
+        lib = _lib.load()
+        dt, dev = q_nope.dtype, q_nope.device
+        S = q_nope.shape[0]
+        T = kv_cache.shape[0]
+        idx = _index32(topk_idx)
+        k = idx.shape[1]
+        _require(q_nope, "q_nope", (S, N_HEADS, D_NOPE), dt, dev)
+        _require(q_pe, "q_pe", (S, N_HEADS, D_ROPE), dt, dev)
+        _require(kv_cache, "kv_cache", (T, D_LATENT), dt, dev)
+        _require(pe_cache, "pe_cache", (T, D_ROPE), dt, dev)
+        _require(idx, "topk_idx", (S, k), torch.int32, dev)
+        _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), dt, dev)
+        _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), dt, dev)
+        if out is None:
+            out = torch.empty((S, N_HEADS, D_V), dtype=dt, device=dev)
+        _require(out, "out", (S, N_HEADS, D_V), dt, dev)
+        code = _dtype_code(dt)
+        need = lib.mla_sparse_prefill_explicit_workspace_size(S, T, k, int(start_pos), code)
+        if need == 0:
+            raise MLAError(2 if code == MLA_BF16 else 4, "mla_sparse_prefill_explicit_workspace_size")
+        ws = _workspace(need, dev, workspace)
+        st = lib.mla_sparse_prefill_explicit(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(pe_cache),
+                                             _ptr(idx), _ptr(w_uk), _ptr(w_uv), _ptr(out), S, T, k,
+                                             int(start_pos), float(softmax_scale), code, _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream))
+        _lib.check(st, "mla_sparse_prefill_explicit")
+        return out
 
 
 def validate_indices(topk_idx, T: int, allow_pad: bool = False, stream=None) -> int:

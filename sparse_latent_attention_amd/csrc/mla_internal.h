@@ -80,6 +80,18 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s, hipEvent_t start = 
 hipError_t launch_uv_f32(const float* o_part, const float* m_part, const float* l_part,
                          const void* w_uv, void* out, int R, int n_split, hipStream_t s);
 
+// Explicit-form sparse prefill (mla_sparse_prefill_explicit): workspace =
+// up-projected keys/values [Tv, 128, 256] bf16, then the selection bitmap
+// [S, words] (32 positions per word), Tv = min(start_pos + S, T).
+struct ExplicitPlan {
+    int Tv, words;
+    size_t up_bytes, bm_off, total;
+};
+ExplicitPlan plan_explicit(int S, int T, int start_pos);
+hipError_t launch_explicit_prefill(const void* q_nope, const void* q_pe, const void* kv, const void* pe,
+                                   const int32_t* idx, const void* w_uk, const void* w_uv, void* out, int S, int k,
+                                   int start_pos, float scale_log2, const ExplicitPlan& p, void* ws, hipStream_t s);
+
 // Output projection (mla_output_projection): [B, 16384] . [7168, 16384]^T.
 constexpr int kProjIn = kHeads * kValue;   // 16,384 joined head outputs
 constexpr int kProjOut = 7168;             // model width

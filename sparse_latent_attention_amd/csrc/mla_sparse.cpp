@@ -214,6 +214,35 @@ mla_status mla_cache_append(const void* kv_a_out, const void* norm_weight, const
                : MLA_ERR_HIP;
 }
 
+size_t mla_sparse_prefill_explicit_workspace_size(int S, int T, int k, int start_pos, int dtype) {
+    if (dtype != MLA_BF16 || S < 1 || T < 1 || T > kMaxT || k < 1 || start_pos < 0 ||
+        (long long)start_pos + S > T)
+        return 0;
+    return plan_explicit(S, T, start_pos).total;
+}
+
+mla_status mla_sparse_prefill_explicit(const void* q_nope, const void* q_pe, const void* kv_cache,
+                                       const void* pe_cache, const int32_t* topk_idx, const void* w_uk,
+                                       const void* w_uv, void* out, int S, int T, int k, int start_pos,
+                                       float softmax_scale, int dtype, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    if (!q_nope || !q_pe || !kv_cache || !pe_cache || !topk_idx || !w_uk || !w_uv || !out) return MLA_ERR_NULL;
+    if (dtype != MLA_BF16) return MLA_ERR_DTYPE;   // bf16 only
+    if (S < 1 || T < 1 || T > kMaxT || k < 1 || start_pos < 0 || (long long)start_pos + S > T)
+        return MLA_ERR_SHAPE;
+    if (!std::isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_cache) || !aligned16(pe_cache) ||
+        !aligned16(topk_idx) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(out))
+        return MLA_ERR_ALIGN;
+    const ExplicitPlan p = plan_explicit(S, T, start_pos);
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < p.total)
+        return MLA_ERR_WORKSPACE;
+    return launch_explicit_prefill(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, out, S, k, start_pos,
+                                   softmax_scale * 1.4426950408889634f, p, workspace, stream) == hipSuccess
+               ? MLA_OK
+               : MLA_ERR_HIP;
+}
+
 mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype, hipStream_t stream) {
     if (!o || !w_o || !out) return MLA_ERR_NULL;
     if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;

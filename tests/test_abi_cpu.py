@@ -217,3 +217,46 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "absent.so"))
+
+
+def call_explicit(lib, **kw):
+    args = dict(q_nope=FAKE, q_pe=FAKE, kv=FAKE, pe=FAKE, idx=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE,
+                S=4, T=100, k=10, start=0, scale=0.07, dtype=1, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.mla_sparse_prefill_explicit(args["q_nope"], args["q_pe"], args["kv"], args["pe"],
+                                           args["idx"], args["w_uk"], args["w_uv"], args["out"],
+                                           args["S"], args["T"], args["k"], args["start"],
+                                           args["scale"], args["dtype"], args["ws"],
+                                           args["ws_bytes"], args["stream"])
+
+
+def test_explicit_prefill_workspace_plan(lib):
+    """Up-projected keys and values of the visible positions, then one bitmap word per 32."""
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    def expected(S, T, start):
+        tv = min(start + S, T)
+        return up(tv * 128 * 256 * 2) + up(S * ((tv + 31) // 32) * 4)
+
+    size = lib.mla_sparse_prefill_explicit_workspace_size
+    assert size(4096, 4096, 2048, 0, 1) == expected(4096, 4096, 0)
+    assert size(3, 100, 10, 50, 1) == expected(3, 100, 50)
+    assert size(1, 1, 1, 0, 1) == expected(1, 1, 0)
+    for bad in [(4, 100, 10, 0, 0), (0, 100, 10, 0, 1), (4, 100, 0, 0, 1), (4, 100, 10, -1, 1),
+                (4, 100, 10, 97, 1), (4, 0, 10, 0, 1)]:
+        assert size(*bad) == 0, bad
+
+
+def test_explicit_prefill_argument_checks(lib):
+    for field in ["q_nope", "q_pe", "kv", "pe", "idx", "w_uk", "w_uv", "out"]:
+        assert call_explicit(lib, **{field: None}) == 1
+        assert call_explicit(lib, **{field: MISALIGNED}) == 3
+    assert call_explicit(lib, dtype=0) == 4           # float32 has no explicit form here
+    for kw in [dict(S=0), dict(T=0), dict(k=0), dict(start=-1), dict(start=97),
+               dict(scale=float("nan"))]:
+        assert call_explicit(lib, **kw) == 2, kw
+    need = lib.mla_sparse_prefill_explicit_workspace_size(4, 100, 10, 0, 1)
+    assert call_explicit(lib, ws_bytes=need - 1) == 5
+    assert call_explicit(lib, ws=None, ws_bytes=need) == 5
+    assert call_explicit(lib, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == 5
