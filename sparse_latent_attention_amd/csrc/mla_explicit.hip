@@ -14,6 +14,8 @@
 // once per block rather than once per (query, position); the price is that
 // the attention visits every position up to the block's last one, selected
 // or not (the dense causal region and half of the rest at the chunk shape).
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -32,130 +34,252 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 }
 
 // --------------------------------------------------------------------------
-// 1. Up-projection.  Workgroup = (block of 64 positions, head h); output
-// [64 t x 256 j] computed transposed, D[j][t] = sum_c W[j][c] c_t[c], with
-// the head's stacked weights (j < 128: W_UK[h][j], else W_UV[h][j - 128]) as
-// the A operand and the latent rows as the B operand, both read straight
-// from memory (16 bytes per lane and k-step).  Wave w takes positions
-// 32 (w % 2) .. +31 and rows j = 128 (w / 2) .. +127 (four 32-row blocks);
-// the next four k-steps' operands are in flight while four are multiplied.
+// Workgroup order.  Workgroups go to the eight XCDs in turn (linear id mod 8),
+// and each XCD has its own L2.  `xcd_tile` deals the linear id so that the
+// blocks of one head run on one XCD, one head after another: that head's
+// weights (up-projection) or keys and values (attention) are then read from
+// HBM about once per XCD and from its L2 after that.  Within a head, blocks
+// are taken last first (the longest causal blocks start earliest).
 // --------------------------------------------------------------------------
-constexpr int kUpChunk = 4;
+__device__ __forceinline__ void xcd_tile(int nblk, int& head, int& blk) {
+    const int L = blockIdx.x;
+    const int i = L >> 3;                                 // position within its XCD's queue
+    head = (kHeads / 8) * (L & 7) + i / nblk;
+    blk = nblk - 1 - i % nblk;
+}
 
-__global__ __launch_bounds__(256) void upproject_bf16(const __bf16* __restrict__ kv, const __bf16* __restrict__ w_uk,
-                                                      const __bf16* __restrict__ w_uv, __bf16* __restrict__ up,
-                                                      int Tv) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = blockIdx.y;
-    const int t0 = blockIdx.x * 64 + 32 * (wave & 1);
-    const int jhalf = wave >> 1;                          // 0: W_UK rows, 1: W_UV rows
-    const int r = lane & 31, half = lane >> 5;
-    const int t = min(t0 + r, Tv - 1);
-    const __bf16* xrow = kv + (size_t)t * kLatent + 8 * half;
-    const __bf16* wbase = (jhalf ? w_uv : w_uk) + ((size_t)h * kNope + r) * kLatent + 8 * half;
-    f32x16 acc[4] = {};
-    bf16x8 A[kUpChunk][4], X[kUpChunk];
-    auto load = [&](int ks, bf16x8 (&a)[4], bf16x8& x) {
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) a[jb] = *reinterpret_cast<const bf16x8*>(wbase + (size_t)32 * jb * kLatent + 16 * ks);
-        x = *reinterpret_cast<const bf16x8*>(xrow + 16 * ks);
+// --------------------------------------------------------------------------
+// 1. Up-projection, a GEMM per head: D[j][t] = sum_c W[j][c] c_t[c] for the
+// 256 rows j of the head's stacked weights (j < 128: W_UK[h][j], else
+// W_UV[h][j - 128]) and a block of 256 positions t.  Weights are the A
+// operand, latent rows the B operand.  Eight waves; wave w computes
+// positions 64 (w / 2) .. +63 and rows 128 (w % 2) .. +127: 2 x 4 MFMA
+// blocks of 32 x 32, 8 MFMAs against 6 16-byte LDS reads per 16 latent
+// columns.  32 columns at a time are staged in LDS (two stages); each
+// thread's share of a chunk comes from memory two chunks ahead, through two
+// register sets, so a chunk has two chunks' worth of MFMA time to arrive.
+// --------------------------------------------------------------------------
+constexpr int kUpT = 256;                 // positions per workgroup
+constexpr int kUpThreads = 512;
+constexpr int kUpC = 32;                  // latent columns per stage
+constexpr int kUpStride = 40;             // bf16 per staged row (32 + pad): conflict-free 16-byte reads
+constexpr int kUpWBytes = 256 * kUpStride * 2;
+constexpr int kUpXBytes = kUpT * kUpStride * 2;
+constexpr int kUpStage = kUpWBytes + kUpXBytes;
+constexpr int kUpChunks = kLatent / kUpC;
+
+__global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __restrict__ kv,
+                                                                const __bf16* __restrict__ w_uk,
+                                                                const __bf16* __restrict__ w_uv,
+                                                                __bf16* __restrict__ up, int Tv, int nblk) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kUpStage];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 31, g = lane >> 5;
+    int h, blk;
+    xcd_tile(nblk, h, blk);
+    const int t0 = blk * kUpT;
+
+    // staging: thread tid moves columns 8 (tid % 4) .. +7 of a chunk for weight rows prow
+    // (W_UK) and 128 + prow (W_UV), and for latent rows t0 + prow and t0 + 128 + prow
+    const int prow = tid >> 2, pcol = 8 * (tid & 3);
+    const __bf16* wk = w_uk + ((size_t)h * kNope + prow) * kLatent + pcol;
+    const __bf16* wv = w_uv + ((size_t)h * kValue + prow) * kLatent + pcol;
+    const __bf16* x0 = kv + (size_t)min(t0 + prow, Tv - 1) * kLatent + pcol;
+    const __bf16* x1 = kv + (size_t)min(t0 + 128 + prow, Tv - 1) * kLatent + pcol;
+    auto gload = [&](int c, u32x4 (&v)[4]) {
+        v[0] = *reinterpret_cast<const u32x4*>(wk + c * kUpC);
+        v[1] = *reinterpret_cast<const u32x4*>(wv + c * kUpC);
+        v[2] = *reinterpret_cast<const u32x4*>(x0 + c * kUpC);
+        v[3] = *reinterpret_cast<const u32x4*>(x1 + c * kUpC);
     };
+    auto sstore = [&](int stage, const u32x4 (&v)[4]) {
+        unsigned char* base = lds + stage * kUpStage + (prow * kUpStride + pcol) * 2;
+        *reinterpret_cast<u32x4*>(base) = v[0];
+        *reinterpret_cast<u32x4*>(base + 128 * kUpStride * 2) = v[1];
+        *reinterpret_cast<u32x4*>(base + kUpWBytes) = v[2];
+        *reinterpret_cast<u32x4*>(base + kUpWBytes + 128 * kUpStride * 2) = v[3];
+    };
+
+    f32x16 acc[2][4] = {};
+    const int jw = 128 * (wave & 1), tw = 64 * (wave >> 1);
+    auto compute = [&](int stage) {
+        const __bf16* wl = reinterpret_cast<const __bf16*>(lds + stage * kUpStage) + (jw + r) * kUpStride + 8 * g;
+        const __bf16* xl = reinterpret_cast<const __bf16*>(lds + stage * kUpStage + kUpWBytes) +
+                           (tw + r) * kUpStride + 8 * g;
 #pragma unroll
-    for (int u = 0; u < kUpChunk; ++u) load(u, A[u], X[u]);
-    for (int c = 0; c < kLatent / 16; c += kUpChunk) {
-        bf16x8 nA[kUpChunk][4], nX[kUpChunk];
-        const bool more = c + kUpChunk < kLatent / 16;
-        if (more) {
+        for (int ks = 0; ks < kUpC / 16; ++ks) {
+            bf16x8 A[4], X[2];
 #pragma unroll
-            for (int u = 0; u < kUpChunk; ++u) load(c + kUpChunk + u, nA[u], nX[u]);
+            for (int jb = 0; jb < 4; ++jb) A[jb] = *reinterpret_cast<const bf16x8*>(wl + 32 * jb * kUpStride + 16 * ks);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) X[tb] = *reinterpret_cast<const bf16x8*>(xl + 32 * tb * kUpStride + 16 * ks);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) acc[tb][jb] = mfma(A[jb], X[tb], acc[tb][jb]);
         }
-#pragma unroll
-        for (int u = 0; u < kUpChunk; ++u)
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) acc[jb] = mfma(A[u][jb], X[u], acc[jb]);
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < kUpChunk; ++u) {
-                X[u] = nX[u];
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) A[u][jb] = nA[u][jb];
-            }
-        }
+    };
+    // chunk c: staged at the top of step c - 1 from the register set it was loaded into
+    // at step c - 3 (c - 2 for the first chunks); that set is then reloaded with chunk c + 2.
+    // The loop body is branch-free (past the end the last chunk is loaded again and staged
+    // into a stage nobody reads), so the compiler's memory-counter waits see both register
+    // sets in flight and wait for the older one only.
+    // The prologue leaves the sets in the loop's order (chunk 1 in set 1 issued before chunk 2
+    // in set 0, and the scheduler kept from mixing the two).
+    u32x4 s0[4], s1[4];
+    gload(0, s0);
+    sstore(0, s0);
+    gload(1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(2, s0);
+    __syncthreads();
+    static_assert(kUpChunks % 2 == 0, "chunks are taken in pairs");
+#pragma unroll 1
+    for (int c = 0; c < kUpChunks; c += 2) {
+        // even step: chunk c+1 from set 1 to stage 1, set 1 <- chunk c+3; multiply stage 0
+        sstore(1, s1);
+        gload(min(c + 3, kUpChunks - 1), s1);
+        compute(0);
+        __syncthreads();
+        // odd step: chunk c+2 from set 0 to stage 0, set 0 <- chunk c+4; multiply stage 1
+        sstore(0, s0);
+        gload(min(c + 4, kUpChunks - 1), s0);
+        compute(1);
+        __syncthreads();
     }
-    // lane (t = lane % 32, g = lane / 32) holds j = 32 jb + 8 (i / 4) + 4 g + i % 4
-    if (t0 + r < Tv) {
-        __bf16* dst = up + ((size_t)(t0 + r) * kHeads + h) * (2 * kNope) + 128 * jhalf + 4 * half;
+    // lane (t = lane % 32, g) holds j = 32 jb + 8 (i / 4) + 4 g + i % 4 of position 32 tb + t
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = t0 + tw + 32 * tb + r;
+        if (t >= Tv) continue;
+        __bf16* dst = up + ((size_t)t * kHeads + h) * (2 * kNope) + jw + 4 * g;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int q4 = 0; q4 < 4; ++q4) {
                 bf16x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[jb][4 * g + e];
-                *reinterpret_cast<bf16x4*>(dst + 32 * jb + 8 * g) = v;
+                for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[tb][jb][4 * q4 + e];
+                *reinterpret_cast<bf16x4*>(dst + 32 * jb + 8 * q4) = v;
             }
     }
 }
 
 // --------------------------------------------------------------------------
-// 2. Selection bitmap [S][words], words = ceil(Tv / 32).
+// 2. Selection bitmap [S][words], words = ceil(Tv / 32).  Workgroup = one
+// query: its words are built in LDS (kBmChunk words = 262,144 positions at a
+// time; one pass below that) with LDS atomics, then written out whole, so no
+// separate clear is needed.  A listed position counts iff 0 <= t < Tv and
+// t <= start_pos + s.
 // --------------------------------------------------------------------------
-__global__ void bitmap_clear(unsigned* bm, long long n) {
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
-        bm[i] = 0u;
+constexpr int kBmChunk = 8192;
+
+__global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ idx, unsigned* __restrict__ bm, int k,
+                                                    int words, int Tv, int start_pos) {
+    __shared__ unsigned w[kBmChunk];
+    const int s = blockIdx.x;
+    const int limit = min(Tv - 1, start_pos + s);
+    const int32_t* row = idx + (size_t)s * k;
+    for (int w0 = 0; w0 < words; w0 += kBmChunk) {
+        const int n = min(kBmChunk, words - w0);
+        for (int i = threadIdx.x; i < n; i += 256) w[i] = 0u;
+        __syncthreads();
+        for (int e = threadIdx.x; e < k; e += 256) {
+            const int t = row[e];
+            if (t < 0 || t > limit) continue;             // empty slot, past the cache or after the query
+            const int wi = (t >> 5) - w0;
+            if (wi >= 0 && wi < n) atomicOr(&w[wi], 1u << (t & 31));
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += 256) bm[(size_t)s * words + w0 + i] = w[i];
+        __syncthreads();
+    }
 }
 
-__global__ void bitmap_set(const int32_t* __restrict__ idx, unsigned* bm, int S, int k, int words, int Tv,
-                           int start_pos) {
-    const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (long long)S * k) return;
-    const int s = (int)(e / k);
-    const int t = idx[e];
-    if (t < 0 || t >= Tv || t > start_pos + s) return;    // empty slot, past the cache or after the query
-    atomicOr(&bm[(size_t)s * words + (t >> 5)], 1u << (t & 31));
-}
-
 // --------------------------------------------------------------------------
-// 3. Attention.  Workgroup = (block of 128 queries, head h); wave w owns
-// queries 32w .. 32w+31 of the block.  Per tile of 32 positions:
+// 3. Attention.  Workgroup = (block of 128 queries, head h), dealt by
+// xcd_tile; wave w owns queries 32w .. 32w+31 of the block.  Per tile of 32
+// positions:
 //   scores  S^T[t][q] = sum_d K[t][d] Q[q][d] (12 MFMAs, k = 192): K from LDS
 //           as the A operand, the wave's queries in registers as B; lane
 //           (q, g) ends up with rows t = 8 (i / 4) + 4 g + i % 4;
-//   mask    bit clear -> -inf (queries past S have no bits);
-//   softmax per query, online: running maximum m and sum l, the accumulator
-//           and l scaled by 2^(m_old - m_new) on every tile (64 multiplies);
-//   mix     O^T[v][q] += sum_t V^T[v][t] P^T[t][q] (8 MFMAs): the
-//           probabilities, packed to bf16 where the scores are, are the B
-//           operand once k slot 8 g' + e stands for row 4 g' + e (e < 4) or
-//           8 + 4 g' + e - 4 (e >= 4) of the k-step's 16; V is stored
-//           transposed in LDS, so each lane reads those rows of its value
-//           column as two 8-byte pieces.
-// K/V tiles are staged through LDS by all 256 threads, three in flight.
+//   weights p = 2^(s * scale * log2(e) - m) where the bit of (q, t) is set,
+//           else 0, against a fixed reference m per query: the maximum of
+//           its scaled scores over the first tile's 32 positions, selected
+//           or not.  The accumulator is never rescaled;
+//   mix     O^T[v][q] += sum_t V^T[v][t] P^T[t][q] (8 MFMAs): the weights,
+//           packed to bf16 where the scores are, are the B operand once k
+//           slot 8 g' + e stands for row 4 g' + e (e < 4) or 8 + 4 g' + e - 4
+//           (e >= 4) of the k-step's 16; V is staged row-major and read as
+//           the A operand with the transposing LDS read (lane i of a 16-lane
+//           block receives column c + i of the four rows its block's lanes
+//           address, lane 4e + q addressing row r_e, columns c + 4q ..).
+// A reference that is too low lets weights grow: any query whose weight sum
+// exceeds 2^64 (or is not finite) makes the whole workgroup start again from
+// an exact reference (a pass that computes only the masked maximum, then the
+// weighted pass against it, whose largest weight is exactly 1).  So does a
+// reference far above every selected score (a query with a selection and a
+// weight sum below 2^-60), where weights would lose range.  Neither happens
+// with scores of moderate spread; the common path has no branch.
+// The scores of tile kt+1 are issued before the weights of tile kt, so the
+// matrix cores work while the vector units do the exponentials.  Tiles pass
+// through three LDS stages (kt: values and bitmap words, kt+1: keys, kt+2:
+// being written) and two register sets (tiles kt+3 and kt+4 in flight).
 // --------------------------------------------------------------------------
 constexpr int kQb = 128;                  // queries per workgroup
 constexpr int kKStride = 200;             // bf16 per staged key row (192 + pad)
-constexpr int kVStride = 40;              // bf16 per staged transposed value row (32 + pad)
+constexpr int kVRow = 144;                // bf16 per staged value row (128 + pad: the four rows of a
+                                          // transposing read fall in disjoint banks)
 constexpr int kKBytes = 32 * kKStride * 2;
-constexpr int kVBytes = 128 * kVStride * 2;
-constexpr int kStage = kKBytes + kVBytes;
+constexpr int kVBytes = 32 * kVRow * 2;
+constexpr int kBitsBytes = kQb * 4;       // each query's bitmap word for the tile
+constexpr int kStage = kKBytes + kVBytes + kBitsBytes;
 constexpr int kStages = 3;
+constexpr float kSumHigh = 18446744073709551616.f;   // 2^64
+constexpr float kSumLow = 8.673617379884035e-19f;    // 2^-60
+
+__device__ __forceinline__ float pair_max(float x) {   // max over lanes l and l ^ 32
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {   // sum over lanes l and l ^ 32
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// Transposing read of four bf16 (see the mix above).
+__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+struct TileRegs {
+    u32x4 v[5];
+    unsigned bits;
+};
 
 __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restrict__ q_nope,
                                                           const __bf16* __restrict__ q_pe,
                                                           const __bf16* __restrict__ up,
                                                           const __bf16* __restrict__ pe,
                                                           const unsigned* __restrict__ bm, __bf16* __restrict__ out,
-                                                          int S, int Tv, int words, int start_pos, float scale_log2) {
+                                                          int S, int Tv, int words, int start_pos, float scale_log2,
+                                                          int nqb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * kStage];
+    __shared__ int rerun_vote[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane & 31, g = lane >> 5;
-    const int h = blockIdx.y;
-    const int qb0 = blockIdx.x * kQb;
+    int h, qblk;
+    xcd_tile(nqb, h, qblk);
+    const int qb0 = qblk * kQb;
     const int qs = qb0 + 32 * wave + q;                   // this lane's query
     const bool qvalid = qs < S;
     // positions any query of the block can see: 0 .. start_pos + last query
     const int last_q = min(qb0 + kQb, S) - 1;
     const int ntiles = (min(start_pos + last_q + 1, Tv) + 31) / 32;
+    const int last = ntiles - 1;
 
     // query fragments: Q[q][16 ks + 8 g .. +7], ks < 8 from q_nope, else q_pe
     bf16x8 qf[12];
@@ -169,9 +293,11 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
         for (int ks = 0; ks < 4; ++ks) qf[8 + ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
     }
 
-    // Stage tile kt: thread tid takes row tid / 8 and 16-byte chunks tid % 8 + 8 i of its
-    // 40 (16 key-content, 8 rotary, 16 value).
-    auto load_tile = [&](int kt, u32x4 (&v)[5]) {
+    // Tile kt to registers: thread tid takes row tid / 8 and 16-byte chunks tid % 8 + 8 i of
+    // its 40 (16 key-content, 8 rotary, 16 value) and query qb0 + tid % 128's bitmap word (a
+    // query past S reads the last one's; its lanes ignore it).
+    auto load_tile = [&](int kt, TileRegs& r) {
+        r.bits = bm[(size_t)min(qb0 + (tid & (kQb - 1)), S - 1) * words + kt];
         const int row = tid >> 3, c0 = tid & 7;
         const int t = min(kt * 32 + row, Tv - 1);
         const __bf16* kvrow = up + ((size_t)t * kHeads + h) * (2 * kNope);
@@ -180,93 +306,143 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
         for (int i = 0; i < 5; ++i) {
             const int c = c0 + 8 * i;                     // 0..15 key, 16..23 rotary, 24..39 value
             const __bf16* src = c < 16 ? kvrow + 8 * c : c < 24 ? perow + 8 * (c - 16) : kvrow + kNope + 8 * (c - 24);
-            v[i] = *reinterpret_cast<const u32x4*>(src);
+            r.v[i] = *reinterpret_cast<const u32x4*>(src);
         }
     };
-    auto store_tile = [&](int stage, const u32x4 (&v)[5]) {
+    auto store_tile = [&](int stage, const TileRegs& r) {
         unsigned char* kb = lds + stage * kStage;
-        __bf16* vt = reinterpret_cast<__bf16*>(kb + kKBytes);
         const int row = tid >> 3, c0 = tid & 7;
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int c = c0 + 8 * i;
-            if (c < 24) {
-                *reinterpret_cast<u32x4*>(kb + (row * kKStride + 8 * c) * 2) = v[i];
+            unsigned char* dst = c < 24 ? kb + (row * kKStride + 8 * c) * 2
+                                        : kb + kKBytes + (row * kVRow + 8 * (c - 24)) * 2;
+            *reinterpret_cast<u32x4*>(dst) = r.v[i];
+        }
+        reinterpret_cast<unsigned*>(kb + kKBytes + kVBytes)[tid & (kQb - 1)] = r.bits;   // twice, same value
+    };
+    // scores: A = K[t][16 ks + 8 g' .. +7] for t = lane % 32
+    auto scores = [&](int stage) {
+        f32x16 sc = {};
+        const __bf16* krow = reinterpret_cast<const __bf16*>(lds + stage * kStage) + q * kKStride + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 12; ++ks) sc = mfma(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], sc);
+        return sc;
+    };
+    // transposing-read addresses: lane (v = 32 vb + lane % 32, g) of a 16-lane block
+    // addresses row 4 g + (lane % 16) / 4 (+ 8 for the second half of a k-step, + 16 kc)
+    // and columns 32 vb + 16 ((lane / 16) % 2) + 4 (lane % 4) ..
+    const int tr_off = ((4 * g + ((lane & 15) >> 2)) * kVRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+    f32x16 acc[4];
+    float l_run, m_ref, m_max;
+    unsigned sel_or;
+
+    // One pass over the block's tiles.  kMaxOnly: the masked maximum of the scaled scores
+    // (m_max); otherwise the weights against m_ref (taken from the first tile if
+    // kFirstRef), their sum (l_run) and the mix (acc).
+    auto pass = [&](auto max_only, auto first_ref) {
+        constexpr bool kMaxOnly = decltype(max_only)::value;
+        constexpr bool kFirstRef = decltype(first_ref)::value;
+        f32x16 s_cur;
+        auto finish_tile = [&](int kt) {
+            const unsigned char* kb = lds + (kt % kStages) * kStage;
+            const unsigned word = reinterpret_cast<const unsigned*>(kb + kKBytes + kVBytes)[32 * wave + q];
+            const unsigned bits = qvalid ? word >> (4 * g) : 0u;
+            if constexpr (kMaxOnly) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = 8 * (i >> 2) + (i & 3);
+                    m_max = (bits >> t) & 1u ? fmaxf(m_max, s_cur[i] * scale_log2) : m_max;
+                }
             } else {
-                const bf16x8 x = __builtin_bit_cast(bf16x8, v[i]);
+                sel_or |= bits;
+                bf16x8 pb[2];
+                float psum = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vt[(8 * (c - 24) + e) * kVStride + row] = x[e];
+                for (int i = 0; i < 16; ++i) {
+                    const int t = 8 * (i >> 2) + (i & 3);
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], scale_log2, -m_ref));
+                    const float p = (bits >> t) & 1u ? e : 0.f;
+                    psum += p;
+                    pb[i >> 3][i & 7] = (__bf16)p;
+                }
+                l_run += psum;
+                const unsigned char* vb0 = kb + kKBytes + tr_off;
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int vb = 0; vb < 4; ++vb) {
+                        const unsigned char* a0 = vb0 + (16 * kc * kVRow + 32 * vb) * 2;
+                        const bf16x8 a = cat(lds_read_tr(a0), lds_read_tr(a0 + 8 * kVRow * 2));
+                        acc[vb] = mfma(a, pb[kc], acc[vb]);
+                    }
             }
+        };
+        // Step kt: tile kt+2 from its register set to LDS, that set <- tile kt+4, scores of
+        // tile kt+1, weights and mix of tile kt.  Branch-free, so that the compiler's memory-
+        // counter waits see both register sets in flight: past the last tile the last one is
+        // loaded and staged again into a stage nobody reads, and the scores beyond it are
+        // dropped.
+        auto step = [&](int kt, TileRegs& set) {
+            store_tile((kt + 2) % kStages, set);
+            load_tile(min(kt + 4, last), set);
+            const f32x16 s_next = scores((kt + 1) % kStages);
+            finish_tile(kt);
+            s_cur = s_next;
+            __syncthreads();                              // stage kt free; stage kt+2 complete
+        };
+        // The prologue leaves tiles 2 and 3 in flight in the loop's order (set ra's loads
+        // first, the scheduler kept from mixing the two sets).
+        TileRegs ra, rb;                                  // tiles 2j and 2j+1
+        load_tile(0, ra);
+        load_tile(min(1, last), rb);
+        store_tile(0, ra);
+        store_tile(1, rb);
+        load_tile(min(2, last), ra);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(min(3, last), rb);
+        __syncthreads();
+        s_cur = scores(0);
+        if constexpr (kFirstRef) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[i] * scale_log2);
+            m_ref = pair_max(mx);
         }
+        int kt = 0;
+        for (; kt + 1 < ntiles; kt += 2) {
+            step(kt, ra);
+            step(kt + 1, rb);
+        }
+        if (kt < ntiles) step(kt, ra);
+    };
+    auto clear = [&]() {
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) acc[vb] = f32x16{};
+        l_run = 0.f;
+        sel_or = 0u;
     };
 
-    f32x16 acc[4] = {};
-    float m_run = -INFINITY, l_run = 0.f;
-    // One tile: stage tile kt+1 (held in `nxt`) to LDS, start loading tile kt+2 into `fut`,
-    // then score, mask, softmax and mix tile kt.  The two register sets alternate, so the
-    // loop runs two tiles per trip and every array index is a constant.
-    auto step = [&](int kt, const u32x4 (&nxt)[5], u32x4 (&fut)[5]) {
-        const int stage = kt % kStages;
-        if (kt + 1 < ntiles) store_tile((kt + 1) % kStages, nxt);
-        if (kt + 2 < ntiles) load_tile(kt + 2, fut);
-        const unsigned char* kb = lds + stage * kStage;
-        const __bf16* vt = reinterpret_cast<const __bf16*>(kb + kKBytes);
-
-        // scores: A = K[t][16 ks + 8 g' .. +7] for t = lane % 32
-        f32x16 s = {};
-        const __bf16* krow = reinterpret_cast<const __bf16*>(kb) + q * kKStride + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 12; ++ks) s = mfma(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], s);
-
-        // mask, maximum, probabilities
-        const unsigned bits = qvalid ? bm[(size_t)qs * words + kt] : 0u;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-            s[i] = (bits >> t) & 1u ? s[i] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float neg = m_new == -INFINITY ? 0.f : -m_new;
-        bf16x8 pb[2];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[i] + neg);
-            psum += p;
-            pb[i >> 3][i & 7] = (__bf16)p;
-        }
-        l_run = l_run * f + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb) acc[vb] *= f;
-
-        // mix: A = V^T[v][rows of slots 8 g' + e] for v = 32 vb + lane % 32
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) {
-                const __bf16* vrow = vt + (32 * vb + q) * kVStride + 16 * kc + 4 * g;
-                const bf16x8 a = cat(*reinterpret_cast<const bf16x4*>(vrow), *reinterpret_cast<const bf16x4*>(vrow + 8));
-                acc[vb] = mfma(a, pb[kc], acc[vb]);
-            }
-        __syncthreads();                                  // stage kt free; stage kt+1 complete
-    };
-    u32x4 pa[5], pb2[5];
-    load_tile(0, pa);
-    if (ntiles > 1) load_tile(1, pb2);
-    store_tile(0, pa);
+    clear();
+    pass(std::false_type{}, std::true_type{});
+    float lt = pair_sum(l_run);
+    const bool has_sel = pair_sum(sel_or != 0u ? 1.f : 0.f) > 0.f;
+    const bool bad = !(lt <= kSumHigh) || (has_sel && lt < kSumLow);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;   // every lane takes part
+    if (lane == 0) rerun_vote[wave] = wave_bad;
     __syncthreads();
-    for (int kt = 0; kt < ntiles; kt += 2) {
-        step(kt, pb2, pa);                                // tile kt+1 from pb2, tile kt+2 into pa
-        if (kt + 1 < ntiles) step(kt + 1, pa, pb2);       // tile kt+2 from pa, tile kt+3 into pb2
+    if (rerun_vote[0] | rerun_vote[1] | rerun_vote[2] | rerun_vote[3]) {
+        m_max = -INFINITY;
+        pass(std::true_type{}, std::false_type{});
+        const float mx = pair_max(m_max);
+        m_ref = mx == -INFINITY ? 0.f : mx;               // no selection: every weight is 0 anyway
+        clear();
+        pass(std::false_type{}, std::false_type{});
+        lt = pair_sum(l_run);
     }
 
     // normalise and store: lane (q, g) holds v = 32 vb + 8 (i / 4) + 4 g + i % 4
-    const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qvalid) {
         __bf16* dst = out + ((size_t)qs * kHeads + h) * kValue + 4 * g;
@@ -300,24 +476,19 @@ hipError_t launch_explicit_prefill(const void* q_nope, const void* q_pe, const v
                                    int start_pos, float scale_log2, const ExplicitPlan& p, void* ws, hipStream_t s) {
     __bf16* up = static_cast<__bf16*>(ws);
     unsigned* bm = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + p.bm_off);
-    hipLaunchKernelGGL(upproject_bf16, dim3((p.Tv + 63) / 64, kHeads), dim3(256), 0, s,
+    const int nblk = (p.Tv + kUpT - 1) / kUpT;
+    hipLaunchKernelGGL(upproject_bf16, dim3((unsigned)nblk * kHeads), dim3(kUpThreads), 0, s,
                        static_cast<const __bf16*>(kv), static_cast<const __bf16*>(w_uk),
-                       static_cast<const __bf16*>(w_uv), up, p.Tv);
+                       static_cast<const __bf16*>(w_uv), up, p.Tv, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long nbm = (long long)S * p.words;
-    const long long clear_blocks = (nbm + 255) / 256;
-    hipLaunchKernelGGL(bitmap_clear, dim3((unsigned)(clear_blocks < 4096 ? clear_blocks : 4096)), dim3(256), 0, s,
-                       bm, nbm);
+    hipLaunchKernelGGL(bitmap_build, dim3((unsigned)S), dim3(256), 0, s, idx, bm, k, p.words, p.Tv, start_pos);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long long nidx = (long long)S * k;
-    hipLaunchKernelGGL(bitmap_set, dim3((unsigned)((nidx + 255) / 256)), dim3(256), 0, s, idx, bm, S, k, p.words, p.Tv,
-                       start_pos);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(explicit_attn_bf16, dim3((S + kQb - 1) / kQb, kHeads), dim3(256), 0, s,
+    const int nqb = (S + kQb - 1) / kQb;
+    hipLaunchKernelGGL(explicit_attn_bf16, dim3((unsigned)nqb * kHeads), dim3(256), 0, s,
                        static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_pe), up,
                        static_cast<const __bf16*>(pe), bm, static_cast<__bf16*>(out), S, p.Tv, p.words, start_pos,
-                       scale_log2);
+                       scale_log2, nqb);
     return hipGetLastError();
 }
 

@@ -103,3 +103,37 @@ def test_explicit_prefill_rejects_float32(mla):
     dev = upload(synth.prefill_inputs(cfg))
     with pytest.raises(mla.MLAError):
         run_explicit(mla, dev, cfg.start_pos)
+
+
+def test_explicit_large_logits_restart_from_exact_reference(mla):
+    # With W_UK = 0 the scores are scale * (q_pe . k_R), products of exact bf16 inputs, so a
+    # large scale spreads them over hundreds of log2 units without amplifying any rounding.
+    # Weights against the first tile's maximum then overflow, and every workgroup starts
+    # again from its exact maximum.
+    cfg = PrefillConfig(35, "explicit_big_logits", S=256, T=700, k=160, start_pos=400, dtype="bf16")
+    inp = synth.prefill_inputs(cfg)
+    inp["w_uk"] = np.zeros_like(inp["w_uk"])
+    scale = 10.0
+    out = to_host64(run_explicit(mla, upload(inp), cfg.start_pos, softmax_scale=scale))
+    err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos, scale=scale))
+    log(f"explicit large logits: rel err {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL["bf16"]
+
+
+def test_explicit_reference_far_above_the_selection(mla):
+    # Rotary-key rows 0..31 scaled by 60 give every query a first-tile maximum far above the
+    # scores of the positions it selects (none of 0..31 for most queries), so its weights
+    # against that reference would underflow; the workgroup starts again from the exact
+    # maximum.  The rotary keys enter the scores unprojected, so the scaling adds no rounding.
+    cfg = PrefillConfig(36, "explicit_low_sel", S=128, T=500, k=96, start_pos=372, dtype="bf16")
+    inp = synth.prefill_inputs(cfg)
+    rows = (inp["pe_cache"][:32].astype(np.uint32) << 16).view(np.float32) * 60.0
+    inp["pe_cache"][:32] = (rows.view(np.uint32) >> 16).astype(np.uint16)
+    idx = inp["topk_idx"]
+    idx[4:][idx[4:] < 32] = -1                      # queries 0..3 keep theirs
+    out = to_host64(run_explicit(mla, upload(inp), cfg.start_pos))
+    err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos))
+    log(f"explicit reference above selection: rel err {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL["bf16"]
