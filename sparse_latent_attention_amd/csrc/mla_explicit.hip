@@ -67,6 +67,8 @@ constexpr int kUpWBytes = 256 * kUpStride * 2;
 constexpr int kUpXBytes = kUpT * kUpStride * 2;
 constexpr int kUpStage = kUpWBytes + kUpXBytes;
 constexpr int kUpChunks = kLatent / kUpC;
+constexpr int kUpOutRow = 264;            // bf16 per staged output row (256 + pad)
+static_assert(128 * kUpOutRow * 2 <= 2 * kUpStage, "output staging fits in the operand stages");
 
 __global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __restrict__ kv,
                                                                 const __bf16* __restrict__ w_uk,
@@ -139,29 +141,48 @@ __global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __
         // even step: chunk c+1 from set 1 to stage 1, set 1 <- chunk c+3; multiply stage 0
         sstore(1, s1);
         gload(min(c + 3, kUpChunks - 1), s1);
+        __builtin_amdgcn_sched_barrier(0);               // the loads go out before the MFMAs
         compute(0);
         __syncthreads();
         // odd step: chunk c+2 from set 0 to stage 0, set 0 <- chunk c+4; multiply stage 1
         sstore(0, s0);
         gload(min(c + 4, kUpChunks - 1), s0);
+        __builtin_amdgcn_sched_barrier(0);
         compute(1);
         __syncthreads();
     }
-    // lane (t = lane % 32, g) holds j = 32 jb + 8 (i / 4) + 4 g + i % 4 of position 32 tb + t
+    // Output through LDS, half the positions at a time: lane (t = lane % 32, g) holds
+    // j = 32 jb + 8 (i / 4) + 4 g + i % 4 of position 32 tb + t, written as 8-byte pieces of
+    // staged rows (row stride 132 dwords: the 32 rows of one write fall in distinct banks);
+    // then each position's 512 contiguous bytes go out as 32 16-byte stores, two positions
+    // per store instruction.
+    __bf16* ostage = reinterpret_cast<__bf16*>(lds);
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int t = t0 + tw + 32 * tb + r;
-        if (t >= Tv) continue;
-        __bf16* dst = up + ((size_t)t * kHeads + h) * (2 * kNope) + jw + 4 * g;
+    for (int half = 0; half < 2; ++half) {
+        if ((wave >> 2) == half) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                bf16x4 v;
+                for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[tb][jb][4 * q4 + e];
-                *reinterpret_cast<bf16x4*>(dst + 32 * jb + 8 * q4) = v;
-            }
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        bf16x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[tb][jb][4 * q4 + e];
+                        *reinterpret_cast<bf16x4*>(ostage + (tw - 128 * half + 32 * tb + r) * kUpOutRow + jw + 32 * jb +
+                                                   8 * q4 + 4 * g) = v;
+                    }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < 128 / (kUpThreads / 32); ++pass) {
+            const int row = pass * (kUpThreads / 32) + (tid >> 5);
+            const int t = t0 + 128 * half + row;
+            if (t < Tv)
+                *reinterpret_cast<u32x4*>(up + ((size_t)t * kHeads + h) * (2 * kNope) + 8 * (tid & 31)) =
+                    *reinterpret_cast<const u32x4*>(ostage + row * kUpOutRow + 8 * (tid & 31));
+        }
+        __syncthreads();
     }
 }
 
@@ -235,6 +256,8 @@ constexpr int kVBytes = 32 * kVRow * 2;
 constexpr int kBitsBytes = kQb * 4;       // each query's bitmap word for the tile
 constexpr int kStage = kKBytes + kVBytes + kBitsBytes;
 constexpr int kStages = 3;
+constexpr int kOutRow = 136;              // bf16 per staged output row (128 + pad)
+static_assert(kQb * kOutRow * 2 <= kStages * kStage, "output staging fits in the tile stages");
 constexpr float kSumHigh = 18446744073709551616.f;   // 2^64
 constexpr float kSumLow = 8.673617379884035e-19f;    // 2^-60
 
@@ -276,6 +299,7 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
     const int qb0 = qblk * kQb;
     const int qs = qb0 + 32 * wave + q;                   // this lane's query
     const bool qvalid = qs < S;
+    const unsigned qmask = qvalid ? ~0u : 0u;             // a query past S selects nothing
     // positions any query of the block can see: 0 .. start_pos + last query
     const int last_q = min(qb0 + kQb, S) - 1;
     const int ntiles = (min(start_pos + last_q + 1, Tv) + 31) / 32;
@@ -348,7 +372,7 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
         auto finish_tile = [&](int kt) {
             const unsigned char* kb = lds + (kt % kStages) * kStage;
             const unsigned word = reinterpret_cast<const unsigned*>(kb + kKBytes + kVBytes)[32 * wave + q];
-            const unsigned bits = qvalid ? word >> (4 * g) : 0u;
+            const unsigned bits = (word >> (4 * g)) & qmask;
             if constexpr (kMaxOnly) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -387,6 +411,7 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
         auto step = [&](int kt, TileRegs& set) {
             store_tile((kt + 2) % kStages, set);
             load_tile(min(kt + 4, last), set);
+            __builtin_amdgcn_sched_barrier(0);           // the loads go out before the MFMAs
             const f32x16 s_next = scores((kt + 1) % kStages);
             finish_tile(kt);
             s_cur = s_next;
@@ -442,19 +467,29 @@ __global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restri
         lt = pair_sum(l_run);
     }
 
-    // normalise and store: lane (q, g) holds v = 32 vb + 8 (i / 4) + 4 g + i % 4
+    // Normalise and store through LDS: lane (q, g) holds v = 32 vb + 8 (i / 4) + 4 g + i % 4
+    // of query 32 wave + q, written as 8-byte pieces of staged rows (row stride 68 dwords: the
+    // 32 rows of one write fall in distinct banks); then each query's 256 contiguous bytes go
+    // out as 16 16-byte stores, four queries per store instruction.  Every wave is past the
+    // last barrier of its passes, so the stages are free.
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qvalid) {
-        __bf16* dst = out + ((size_t)qs * kHeads + h) * kValue + 4 * g;
+    __bf16* ostage = reinterpret_cast<__bf16*>(lds);
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                bf16x4 v;
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[vb][4 * gq + e] * inv);
-                *reinterpret_cast<bf16x4*>(dst + 32 * vb + 8 * gq) = v;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[vb][4 * gq + e] * inv);
+            *reinterpret_cast<bf16x4*>(ostage + (32 * wave + q) * kOutRow + 32 * vb + 8 * gq + 4 * g) = v;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < kQb / 16; ++pass) {
+        const int row = pass * 16 + (tid >> 4);
+        if (qb0 + row < S)
+            *reinterpret_cast<u32x4*>(out + ((size_t)(qb0 + row) * kHeads + h) * kValue + 8 * (tid & 15)) =
+                *reinterpret_cast<const u32x4*>(ostage + row * kOutRow + 8 * (tid & 15));
     }
 }
 
