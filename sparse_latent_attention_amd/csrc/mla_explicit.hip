@@ -283,7 +283,7 @@ struct TileRegs {
     unsigned bits;
 };
 
-__global__ __launch_bounds__(256) void explicit_attn_bf16(const __bf16* __restrict__ q_nope,
+__global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __restrict__ q_nope,
                                                           const __bf16* __restrict__ q_pe,
                                                           const __bf16* __restrict__ up,
                                                           const __bf16* __restrict__ pe,
