@@ -44,9 +44,9 @@ Workspace plan_workspace(int rows, int k, int dtype) {
     w.q_off = 0;
     w.q_bytes = R * kHeads * kQRow * esize;
     w.o_off = round_up(w.q_off + w.q_bytes, kAlign);
-    // bf16: per split, the unnormalised mix in bf16 + reference max and sum
-    // (a negative sum marks a head the merge must recompute exactly);
-    // f32: per split, the unnormalised mix in f32 + running max and sum.
+    // bf16: per split, the unnormalised mix in bf16 + the reference maximum and
+    // the sum of weights against it; f32: per split, the unnormalised mix in
+    // f32 + running max and sum.
     const bool bf16 = dtype == MLA_BF16;
     w.o_bytes = (size_t)n * R * kHeads * kLatent * (bf16 ? 2 : 4);
     w.ml_off = round_up(w.o_off + w.o_bytes, kAlign);

@@ -62,6 +62,10 @@ def test_write_traffic_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert rec["algorithmic_bytes_per_launch"] == 64 * 2048 * 1152
     assert rec["kernel_source_sha256_16"] == bench.source_hash()
     assert rec["FETCH_SIZE_kib_uv"] == pytest.approx(26000.0)
+    # the whole call: the three kernels' counters, each scaled like the attention kernel's
+    assert rec["step_bytes_per_call"] == pytest.approx((80000.0 + 26000.0 + 9800.0) * 2048
+                                                       + (33536.0 + 2048.0 + 9216.0) * 1024)
+    assert rec["algorithmic_step_bytes_per_call"] == bench.step_bytes(64, 2048)
 
 
 def test_traffic_record_is_used_only_while_the_code_matches(tmp_path, monkeypatch):
@@ -70,11 +74,18 @@ def test_traffic_record_is_used_only_while_the_code_matches(tmp_path, monkeypatc
     rec_file = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "KERNEL_SOURCES", (str(src),))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec_file))
-    assert bench.traffic_from_profile(1) is None            # no record
+    assert bench.traffic_from_profile() == (None, None)       # no record
     rec_file.write_text(json.dumps({"kernel_source_sha256_16": bench.source_hash(),
-                                    "bytes_per_launch": 123.0}))
-    assert bench.traffic_from_profile(1) == 123.0
+                                    "bytes_per_launch": 123.0, "step_bytes_per_call": 456.0}))
+    assert bench.traffic_from_profile() == (123.0, 456.0)
     src.write_text("int kernel() { return 1; }  // comment edits keep the record\n")
-    assert bench.traffic_from_profile(1) == 123.0
+    assert bench.traffic_from_profile() == (123.0, 456.0)
     src.write_text("int kernel() { return 2; }\n")
-    assert bench.traffic_from_profile(1) is None            # the code changed
+    assert bench.traffic_from_profile() == (None, None)       # the code changed
+
+
+def test_step_bytes_and_flops():
+    # headline call: 131,072 selected rows of 1,152 bytes, two 16 MiB weight matrices,
+    # q_nope + q_pe in and the output out (320 bf16 per row and head), 4-byte indices
+    assert bench.step_bytes(64, 2048) == 150_994_944 + 33_554_432 + 5_242_880 + 524_288
+    assert bench.step_flops(64, 2048) == 131_072 * 2 * 128 * 1088 + 4 * 64 * 128 * 128 * 512
