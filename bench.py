@@ -81,6 +81,8 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="time the prefill chunk (S=T=4096, k=min(t+1, 2048), bf16) instead of decode; "
                         "prints its own JSON line (not the headline metric)")
+    p.add_argument("--append", action="store_true",
+                   help="time the cache append of a 4096-position chunk; prints its own JSON line")
     p.add_argument("--prefill-explicit", action="store_true",
                    help="time the same prefill chunk in the explicit form (keys and values "
                         "up-projected per head); prints its own JSON line")
@@ -360,6 +362,53 @@ def bench_project(args, torch, synth, mla):
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
 
 
+def bench_append(args, torch, synth, mla):
+    """The cache append of 4096-position prefill chunks of 8 sequences (B = 8, S = 4096 into 4096-row caches):
+    per position 576 down-projection outputs read and 576 cache values written, bf16.  The
+    one-position decode append of 64 sequences is timed beside it (a latency figure)."""
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float32:
+            return torch.from_numpy(x).to(dev)
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed(cfg, steps, warm):
+        d = {name: up(v) for name, v in synth.append_inputs(cfg).items()}
+
+        def call():
+            mla.cache_append(d["kv_a_out"], d["norm_weight"], d["cos_sin"], d["kv_cache"], d["pe_cache"],
+                             start_pos=cfg.start_pos)
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps
+
+    from synth.generators import AppendConfig
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    sec = timed(AppendConfig(80, "append_chunk", B=8, S=4096, T=4096, start_pos=0, dtype="bf16"), steps, warm)
+    sec_dec = timed(AppendConfig(81, "append_decode", B=64, S=1, T=64, start_pos=63, dtype="bf16"),
+                    steps, warm)
+    nbytes = 8 * 4096 * (576 + 576) * 2 + 512 * 2 + 4096 * 32 * 2 * 4
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "cache append rate (B=8 x S=4096 positions, bf16)", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic append_inputs",
+        "config": {"workload": "cache append: RMSNorm of 512 latent values, rotation of 64 rotary values, "
+                               "write at start_pos; B=8, S=4096, ld_T=4096, bf16", "bytes": nbytes},
+        "decode_append_b64_ms": sec_dec * 1e3,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +434,9 @@ def main():
         return
     if args.project:
         bench_project(args, torch, synth, mla)
+        return
+    if args.append:
+        bench_append(args, torch, synth, mla)
         return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS["sparse_b64_t32k"]
