@@ -105,6 +105,25 @@ def test_explicit_prefill_rejects_float32(mla):
         run_explicit(mla, dev, cfg.start_pos)
 
 
+def reference_gaps(inp, start_pos, scale, queries, heads):
+    """For sampled (query, head) pairs: the largest selected scaled score (log2 units) minus the
+    first-tile reference (the largest over positions 0..31, selected or not), from the inputs in
+    float64 (the scores' definition)."""
+    kv, pe = oracle.to_f64(inp["kv_cache"]), oracle.to_f64(inp["pe_cache"])
+    w_uk = oracle.to_f64(inp["w_uk"])
+    qn, qp = oracle.to_f64(inp["q_nope"]), oracle.to_f64(inp["q_pe"])
+    T = kv.shape[0]
+    gaps = []
+    for h in heads:
+        k_nope = kv @ w_uk[h].T
+        for s in queries:
+            sc = (k_nope @ qn[s, h] + pe @ qp[s, h]) * scale * np.log2(np.e)
+            sel = oracle.selected_rows(inp["topk_idx"][s], T, start_pos + s)
+            if sel.size:
+                gaps.append(float(sc[sel].max() - sc[:32].max()))
+    return np.array(gaps)
+
+
 def test_explicit_large_logits_restart_from_exact_reference(mla):
     # With W_UK = 0 the scores are scale * (q_pe . k_R), products of exact bf16 inputs, so a
     # large scale spreads them over hundreds of log2 units without amplifying any rounding.
@@ -114,6 +133,9 @@ def test_explicit_large_logits_restart_from_exact_reference(mla):
     inp = synth.prefill_inputs(cfg)
     inp["w_uk"] = np.zeros_like(inp["w_uk"])
     scale = 10.0
+    gaps = reference_gaps(inp, cfg.start_pos, scale, range(0, cfg.S, 37), range(0, 128, 31))
+    log(f"explicit large logits: largest gap over the first-tile reference {gaps.max():.1f} (log2)")
+    assert gaps.max() > 128                         # weights against it would overflow float
     out = to_host64(run_explicit(mla, upload(inp), cfg.start_pos, softmax_scale=scale))
     err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos, scale=scale))
     log(f"explicit large logits: rel err {err:.3e}")
@@ -132,6 +154,9 @@ def test_explicit_reference_far_above_the_selection(mla):
     inp["pe_cache"][:32] = (rows.view(np.uint32) >> 16).astype(np.uint16)
     idx = inp["topk_idx"]
     idx[4:][idx[4:] < 32] = -1                      # queries 0..3 keep theirs
+    gaps = reference_gaps(inp, cfg.start_pos, oracle.SOFTMAX_SCALE, range(4, cfg.S, 13), range(0, 128, 31))
+    log(f"explicit reference above selection: smallest gap {gaps.min():.1f} (log2)")
+    assert gaps.min() < -60                         # weights against it would lose range
     out = to_host64(run_explicit(mla, upload(inp), cfg.start_pos))
     err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos))
     log(f"explicit reference above selection: rel err {err:.3e}")
