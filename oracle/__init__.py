@@ -15,6 +15,7 @@ from .mla_oracle import (  # noqa: F401
     D_QK,
     D_ROPE,
     D_V,
+    FP8_BLOCK,
     N_HEADS,
     SOFTMAX_SCALE,
     absorbed_scores,
@@ -24,6 +25,8 @@ from .mla_oracle import (  # noqa: F401
     decode,
     decode_absorbed,
     explicit_scores,
+    fp8_block_dequant,
+    fp8_e4m3_decode,
     index_mask,
     join_keys,
     join_query,
@@ -38,4 +41,5 @@ from .mla_oracle import (  # noqa: F401
     stack_wkv_b,
     to_f64,
     up_project,
+    wkv_b_dequant,
 )

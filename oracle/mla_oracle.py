@@ -375,3 +375,49 @@ def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
     """
     o = to_f64(o)
     return o.reshape(o.shape[0], N_HEADS * D_V) @ to_f64(w_o).T
+
+
+# --------------------------------------------------------------------------
+# FP8 wkv_b: the decode branch dequantises the stored wkv_b once when it
+# carries a scale and caches the result ("Mix and project", Explanation,
+# decode-branch code); the pages name FP8 block scales ("Key heads",
+# Parameters, the note under the table) but not their format.  Reading:
+# OCP E4M3 codes -- 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+# exponent 0 holds the subnormals m * 2^-9; the code with every exponent and
+# mantissa bit set is NaN; there are no infinities -- and one scale per
+# 128 x 128 block of the [rows, cols] weight.
+# --------------------------------------------------------------------------
+FP8_BLOCK = 128
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 byte, exactly, in float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    # normal: (1 + m/8) * 2^(e - 7) = (8 + m) * 2^(e - 10); subnormal: (m/8) * 2^(1 - 7)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    val = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def fp8_block_dequant(codes: np.ndarray, scales: np.ndarray, block: int = FP8_BLOCK) -> np.ndarray:
+    """weight[r, c] = value(codes[r, c]) * scales[r // block, c // block], float64."""
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    s = to_f64(scales)
+    assert s.shape == (-(-R // block), -(-C // block)), "one scale per block"
+    full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:R, :C]
+    return fp8_e4m3_decode(codes) * full
+
+
+def wkv_b_dequant(codes: np.ndarray, scales: np.ndarray):
+    """The dequantised wkv_b [128 * 256, 512] split per head into W_UK and W_UV.
+
+    The decode branch views the weight as [heads, 256, 512] and takes the first
+    qk_nope_head_dim rows of each head as W_UK and the rest as W_UV ("Mix and
+    project", Explanation, decode-branch code).  Returns two [128, 128, 512].
+    """
+    w = fp8_block_dequant(codes, scales).reshape(N_HEADS, D_NOPE + D_V, D_LATENT)
+    return w[:, :D_NOPE], w[:, D_NOPE:]

@@ -16,6 +16,7 @@ from .generators import (  # noqa: F401
     decode_batch_row,
     decode_inputs,
     decode_query_set,
+    fp8_wkv_b_inputs,
     prefill_inputs,
     prefill_query_rows,
     projection_inputs,

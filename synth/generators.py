@@ -257,3 +257,13 @@ def projection_inputs(B: int, dtype: str, cid: int = 70, seed: int = DEFAULT_SEE
     o = rng.standard_normal((B, N_HEADS, D_V), dtype=np.float32)
     w = rng.standard_normal((D_MODEL, N_HEADS * D_V), dtype=np.float32) * np.float32(1.0 / 128.0)
     return {"o": _store(o, dtype), "w_o": _store(w, dtype)}
+
+
+def fp8_wkv_b_inputs(cid: int = 90, seed: int = DEFAULT_SEED, rows: int = N_HEADS * (D_NOPE + D_V)):
+    """An FP8 wkv_b as the model stores it: codes [rows, 512] (uint8, uniform over the 254 codes
+    that are not NaN) and one float32 scale per 128 x 128 block, log-uniform in [2^-14, 2^-4]."""
+    rng = np.random.default_rng([seed, cid, _TAG_WEIGHTS, 3])
+    codes = rng.integers(0, 254, size=(rows, D_LATENT), dtype=np.int64)
+    codes = codes + (codes >= 0x7F)                      # skip 0x7F; 0xFF is past the range
+    scales = np.exp2(rng.uniform(-14.0, -4.0, size=(-(-rows // 128), D_LATENT // 128)))
+    return {"codes": codes.astype(np.uint8), "scales": scales.astype(np.float32)}

@@ -88,3 +88,14 @@ def test_named_configs_match_stated_shapes():
     p = c["prefill_s4096"]
     assert (p.S, p.T, p.k, p.start_pos) == (4096, 4096, 2048, 0)
     assert sum(p.valid_count(s) for s in range(p.S)) == 6292480
+
+
+def test_fp8_wkv_b_inputs():
+    d = synth.fp8_wkv_b_inputs()
+    c, s = d["codes"], d["scales"]
+    assert c.shape == (128 * 256, 512) and c.dtype == np.uint8
+    assert s.shape == (256, 4) and s.dtype == np.float32
+    assert not np.any((c == 0x7F) | (c == 0xFF))            # no NaN codes
+    assert len(np.unique(c)) == 254
+    assert np.all((s >= 2.0 ** -14) & (s <= 2.0 ** -4))
+    assert np.array_equal(synth.fp8_wkv_b_inputs()["codes"], c)   # seeded
