@@ -81,6 +81,8 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="time the prefill chunk (S=T=4096, k=min(t+1, 2048), bf16) instead of decode; "
                         "prints its own JSON line (not the headline metric)")
+    p.add_argument("--dequant", action="store_true",
+                   help="time the FP8 wkv_b dequantisation; prints its own JSON line")
     p.add_argument("--append", action="store_true",
                    help="time the cache append of a 4096-position chunk; prints its own JSON line")
     p.add_argument("--prefill-explicit", action="store_true",
@@ -409,6 +411,38 @@ def bench_append(args, torch, synth, mla):
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
 
 
+def bench_dequant(args, torch, synth, mla):
+    """The FP8 wkv_b dequantisation: 16.8 MB of E4M3 codes and 4 KB of block scales read,
+    W_UK and W_UV (33.5 MB of bf16) written."""
+    dev = torch.device("cuda:0")
+    d = synth.fp8_wkv_b_inputs()
+    codes = torch.from_numpy(d["codes"]).to(dev)
+    scales = torch.from_numpy(d["scales"]).to(dev)
+    w_uk = torch.empty((128, 128, 512), dtype=torch.bfloat16, device=dev)
+    w_uv = torch.empty_like(w_uk)
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    for _ in range(warm):
+        mla.wkv_b_dequant(codes, scales, w_uk=w_uk, w_uv=w_uv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mla.wkv_b_dequant(codes, scales, w_uk=w_uk, w_uv=w_uv)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = codes.numel() + scales.numel() * 4 + 2 * w_uk.numel() * 2
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "FP8 wkv_b dequantisation rate (32768 x 512 E4M3, 128 x 128 block scales)", "value": gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "dtype": "fp8->bf16", "data": "synthetic fp8_wkv_b_inputs",
+        "config": {"workload": "wkv_b dequantisation: E4M3 codes [32768, 512] x block scales -> "
+                               "W_UK, W_UV [128, 128, 512] bf16", "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -437,6 +471,9 @@ def main():
         return
     if args.append:
         bench_append(args, torch, synth, mla)
+        return
+    if args.dequant:
+        bench_dequant(args, torch, synth, mla)
         return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS["sparse_b64_t32k"]

@@ -174,6 +174,30 @@ MLA_API mla_status mla_output_projection(const void* o, const void* w_o, void* o
                                          hipStream_t stream);
 
 /*
+ * FP8 wkv_b dequantisation: the decode branch dequantises the stored wkv_b
+ * once when it carries a scale, views it [heads, 256, 512] and takes the first
+ * 128 rows of each head as W_UK and the last 128 as W_UV ("Mix and project"
+ * page, Explanation, decode-branch code; FP8 block scales: "Key heads" page,
+ * Parameters, the note under the table).  The pages do not give the format;
+ * this library reads it as OCP E4M3 codes (1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9; the code
+ * with all exponent and mantissa bits set is NaN; no infinities) and one
+ * float32 scale per 128 x 128 block:
+ *
+ *   w[r, c] = value(codes[r, c]) * scales[r / 128, c / 128]
+ *   w_uk[h, d, c] = w[256 h + d, c],  w_uv[h, d, c] = w[256 h + 128 + d, c]
+ *
+ *   codes   [32768, 512] uint8 (16-byte aligned)
+ *   scales  [256, 4] float32, row-major by block
+ *   w_uk, w_uv [128, 128, 512] bf16, written (value times scale in float32,
+ *           rounded once to bf16); the inputs mla_sparse_decode takes
+ *
+ * Errors: MLA_ERR_NULL, MLA_ERR_ALIGN, MLA_ERR_HIP.
+ */
+MLA_API mla_status mla_wkv_b_dequant(const void* codes, const float* scales, void* w_uk, void* w_uv,
+                                     hipStream_t stream);
+
+/*
  * Cache append: the step that fills the caches the attention reads
  * ("KV compression" page, Explanation and code: one joint down-projection
  * gives the 512-wide latent and the 64-wide rotary key, split after the

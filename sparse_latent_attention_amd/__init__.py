@@ -19,7 +19,7 @@ D_MODEL = 7168
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "decode_noalloc", "prefill_chunk", "prefill_explicit", "prefill_explicit_workspace_size", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "prefill_explicit", "prefill_explicit_workspace_size", "wkv_b_dequant", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -298,6 +298,25 @@ def prefill_explicit(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, 
                                              ws.numel() * ws.element_size(), _stream(stream))
         _lib.check(st, "mla_sparse_prefill_explicit")
         return out
+
+
+def wkv_b_dequant(codes, scales, *, w_uk=None, w_uv=None, stream=None):
+    """FP8 wkv_b [32768, 512] (uint8 E4M3 codes) with one float32 scale per 128 x 128 block
+    ([256, 4]) to bf16 W_UK and W_UV [128, 128, 512].  Returns (w_uk, w_uv)."""
+    with _on_stream(stream):
+        lib = _lib.load()
+        dev = codes.device
+        _require(codes, "codes", (N_HEADS * (D_NOPE + D_V), D_LATENT), torch.uint8, dev)
+        _require(scales, "scales", (N_HEADS * (D_NOPE + D_V) // 128, D_LATENT // 128), torch.float32, dev)
+        if w_uk is None:
+            w_uk = torch.empty((N_HEADS, D_NOPE, D_LATENT), dtype=torch.bfloat16, device=dev)
+        if w_uv is None:
+            w_uv = torch.empty((N_HEADS, D_V, D_LATENT), dtype=torch.bfloat16, device=dev)
+        _require(w_uk, "w_uk", (N_HEADS, D_NOPE, D_LATENT), torch.bfloat16, dev)
+        _require(w_uv, "w_uv", (N_HEADS, D_V, D_LATENT), torch.bfloat16, dev)
+        st = lib.mla_wkv_b_dequant(_ptr(codes), _ptr(scales), _ptr(w_uk), _ptr(w_uv), _stream(stream))
+        _lib.check(st, "mla_wkv_b_dequant")
+        return w_uk, w_uv
 
 
 def validate_indices(topk_idx, T: int, allow_pad: bool = False, stream=None) -> int:

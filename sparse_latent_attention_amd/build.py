@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_sparse.so")
-SOURCES = ["mla_sparse.cpp", "mla_bf16.hip", "mla_f32.hip", "mla_noalloc.hip", "mla_append.hip", "mla_project.hip", "mla_explicit.hip"]
+SOURCES = ["mla_sparse.cpp", "mla_bf16.hip", "mla_f32.hip", "mla_noalloc.hip", "mla_append.hip", "mla_project.hip", "mla_explicit.hip", "mla_dequant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -92,6 +92,9 @@ hipError_t launch_explicit_prefill(const void* q_nope, const void* q_pe, const v
                                    const int32_t* idx, const void* w_uk, const void* w_uv, void* out, int S, int k,
                                    int start_pos, float scale_log2, const ExplicitPlan& p, void* ws, hipStream_t s);
 
+// FP8 wkv_b dequantisation (mla_wkv_b_dequant)
+hipError_t launch_wkv_b_dequant(const void* codes, const float* scales, void* w_uk, void* w_uv, hipStream_t s);
+
 // Output projection (mla_output_projection): [B, 16384] . [7168, 16384]^T.
 constexpr int kProjIn = kHeads * kValue;   // 16,384 joined head outputs
 constexpr int kProjOut = 7168;             // model width

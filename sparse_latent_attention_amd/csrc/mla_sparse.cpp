@@ -243,6 +243,13 @@ mla_status mla_sparse_prefill_explicit(const void* q_nope, const void* q_pe, con
                : MLA_ERR_HIP;
 }
 
+mla_status mla_wkv_b_dequant(const void* codes, const float* scales, void* w_uk, void* w_uv, hipStream_t stream) {
+    if (!codes || !scales || !w_uk || !w_uv) return MLA_ERR_NULL;
+    if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0 || !aligned16(w_uk) || !aligned16(w_uv))
+        return MLA_ERR_ALIGN;
+    return launch_wkv_b_dequant(codes, scales, w_uk, w_uv, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype, hipStream_t stream) {
     if (!o || !w_o || !out) return MLA_ERR_NULL;
     if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;

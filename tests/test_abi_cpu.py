@@ -260,3 +260,11 @@ def test_explicit_prefill_argument_checks(lib):
     assert call_explicit(lib, ws_bytes=need - 1) == 5
     assert call_explicit(lib, ws=None, ws_bytes=need) == 5
     assert call_explicit(lib, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == 5
+
+
+def test_wkv_b_dequant_argument_checks(lib):
+    assert lib.mla_wkv_b_dequant(None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_wkv_b_dequant(FAKE, FAKE, None, FAKE, None) == 1
+    assert lib.mla_wkv_b_dequant(MISALIGNED, FAKE, FAKE, FAKE, None) == 3
+    assert lib.mla_wkv_b_dequant(FAKE, ctypes.c_void_p(0x10002), FAKE, FAKE, None) == 3
+    assert lib.mla_wkv_b_dequant(FAKE, FAKE, FAKE, MISALIGNED, None) == 3
