@@ -164,14 +164,20 @@ MLA_API mla_status mla_sparse_prefill_chunk(const void* q_nope, const void* q_pe
  *   w_o  [7168, 16384]  the output layer's weight in its [out, in] storage
  *   out  [B, 7168]      written, never read
  *
- * bf16: MFMA with float32 accumulation, result rounded to bf16; float32:
- * float32 throughout.  Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (B < 1),
- * MLA_ERR_ALIGN, MLA_ERR_DTYPE, MLA_ERR_HIP.
+ * bf16: MFMA with float32 accumulation; the 16,384 inputs are taken in eight
+ * ranges whose float32 partial sums go to the workspace (256-byte aligned,
+ * mla_output_projection_workspace_size(B, dtype) bytes, contents ignored) and
+ * are then added and rounded once to bf16 (deterministic).  float32: float32
+ * throughout, no workspace (size 0; NULL accepted).  Errors: MLA_ERR_NULL,
+ * MLA_ERR_SHAPE (B < 1), MLA_ERR_ALIGN, MLA_ERR_DTYPE, MLA_ERR_WORKSPACE,
+ * MLA_ERR_HIP.
  */
 #define MLA_D_MODEL 7168
 
+MLA_API size_t mla_output_projection_workspace_size(int B, int dtype);
+
 MLA_API mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype,
-                                         hipStream_t stream);
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * FP8 wkv_b dequantisation: the decode branch dequantises the stored wkv_b

@@ -19,7 +19,7 @@ D_MODEL = 7168
 SOFTMAX_SCALE = (D_NOPE + D_ROPE) ** -0.5
 NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # MLA_NOALLOC_SCRATCH_BYTES in include/mla_sparse.h
 
-__all__ = ["decode", "decode_noalloc", "prefill_chunk", "prefill_explicit", "prefill_explicit_workspace_size", "wkv_b_dequant", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
+__all__ = ["decode", "decode_noalloc", "prefill_chunk", "prefill_explicit", "prefill_explicit_workspace_size", "wkv_b_dequant", "output_projection_workspace_size", "cache_append", "output_projection", "decode_workspace_size", "prefill_chunk_workspace_size",
            "validate_indices", "diagnostics", "set_attention_events", "status_string",
            "abi_version",
            "MLAError", "SOFTMAX_SCALE"]
@@ -221,7 +221,11 @@ def prefill_chunk(q_nope, q_pe, kv_cache, pe_cache, topk_idx, w_uk, w_uv, *, sta
         return out
 
 
-def output_projection(o, w_o, *, out=None, stream=None):
+def output_projection_workspace_size(B: int, dtype=torch.bfloat16) -> int:
+    return _lib.load().mla_output_projection_workspace_size(int(B), _dtype_code(dtype))
+
+
+def output_projection(o, w_o, *, out=None, workspace=None, stream=None):
     """Delta = o W_O: o [B, 128, 128] (per-head outputs), w_o [7168, 16384]; returns out [B, 7168]."""
     with _on_stream(stream):
         lib = _lib.load()
@@ -232,7 +236,12 @@ def output_projection(o, w_o, *, out=None, stream=None):
         if out is None:
             out = torch.empty((B, D_MODEL), dtype=dt, device=dev)
         _require(out, "out", (B, D_MODEL), dt, dev)
-        st = lib.mla_output_projection(_ptr(o), _ptr(w_o), _ptr(out), B, _dtype_code(dt), _stream(stream))
+        code = _dtype_code(dt)
+        need = lib.mla_output_projection_workspace_size(B, code)
+        ws = _workspace(need, dev, workspace) if need else None
+        st = lib.mla_output_projection(_ptr(o), _ptr(w_o), _ptr(out), B, code,
+                                       _ptr(ws) if ws is not None else None,
+                                       ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
         _lib.check(st, "mla_output_projection")
         return out
 

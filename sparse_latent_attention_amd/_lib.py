@@ -31,7 +31,8 @@ SIGNATURES = {
     "mla_sparse_prefill_chunk": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _I, _I, _I, _I, _F, _I, _VP, _SZ, _VP]),
     "mla_cache_append": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _F, _I, _VP]),
-    "mla_output_projection": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
+    "mla_output_projection_workspace_size": (_SZ, [_I, _I]),
+    "mla_output_projection": (_I, [_VP, _VP, _VP, _I, _I, _VP, _SZ, _VP]),
     "mla_sparse_prefill_explicit_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "mla_sparse_prefill_explicit": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                          _I, _I, _I, _I, _F, _I, _VP, _SZ, _VP]),

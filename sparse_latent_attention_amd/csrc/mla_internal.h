@@ -98,7 +98,8 @@ hipError_t launch_wkv_b_dequant(const void* codes, const float* scales, void* w_
 // Output projection (mla_output_projection): [B, 16384] . [7168, 16384]^T.
 constexpr int kProjIn = kHeads * kValue;   // 16,384 joined head outputs
 constexpr int kProjOut = 7168;             // model width
-hipError_t launch_project(const void* o, const void* w_o, void* out, int B, bool bf16, hipStream_t s);
+size_t project_workspace_bytes(int B, bool bf16);
+hipError_t launch_project(const void* o, const void* w_o, void* out, int B, bool bf16, void* ws, hipStream_t s);
 
 // Cache append (mla_cache_append): one wave per new position.
 hipError_t launch_cache_append(const void* kv_a_out, const void* norm_weight, const float* cos_sin, void* kv_cache,

@@ -146,7 +146,7 @@ const char* mla_status_string(int s) {
     }
 }
 
-int mla_abi_version(void) { return 2; }
+int mla_abi_version(void) { return 3; }
 
 size_t mla_sparse_decode_workspace_size(int B, int T, int k, int dtype) {
     if (!dtype_ok(dtype) || B < 1 || T < 1 || T > kMaxT || k < 1 || k > T) return 0;
@@ -250,12 +250,23 @@ mla_status mla_wkv_b_dequant(const void* codes, const float* scales, void* w_uk,
     return launch_wkv_b_dequant(codes, scales, w_uk, w_uv, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype, hipStream_t stream) {
+size_t mla_output_projection_workspace_size(int B, int dtype) {
+    if (!dtype_ok(dtype) || B < 1 || (long long)B * kProjOut > 0x7fffffffLL) return 0;
+    return project_workspace_bytes(B, dtype == MLA_BF16);
+}
+
+mla_status mla_output_projection(const void* o, const void* w_o, void* out, int B, int dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
     if (!o || !w_o || !out) return MLA_ERR_NULL;
     if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
     if (B < 1 || (long long)B * kProjOut > 0x7fffffffLL) return MLA_ERR_SHAPE;
     if (!aligned16(o) || !aligned16(w_o) || !aligned16(out)) return MLA_ERR_ALIGN;
-    return launch_project(o, w_o, out, B, dtype == MLA_BF16, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+    const size_t need = project_workspace_bytes(B, dtype == MLA_BF16);
+    if (need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
+                     workspace_bytes < need))
+        return MLA_ERR_WORKSPACE;
+    return launch_project(o, w_o, out, B, dtype == MLA_BF16, workspace, stream) == hipSuccess ? MLA_OK
+                                                                                               : MLA_ERR_HIP;
 }
 
 mla_status mla_read_diagnostics(const void* workspace, int rows, int k, int dtype, int* d_out,

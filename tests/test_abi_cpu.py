@@ -46,7 +46,7 @@ def test_status_strings(lib):
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(code).decode().startswith(name)
     assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
 
 
 def ws_expected(rows, esize, n_split):
@@ -204,11 +204,18 @@ def test_cache_append_argument_checks(lib):
 
 
 def test_output_projection_argument_checks(lib):
-    assert lib.mla_output_projection(None, FAKE, FAKE, 2, 1, None) == 1
-    assert lib.mla_output_projection(FAKE, FAKE, None, 2, 1, None) == 1
-    assert lib.mla_output_projection(FAKE, MISALIGNED, FAKE, 2, 1, None) == 3
-    assert lib.mla_output_projection(FAKE, FAKE, FAKE, 0, 1, None) == 2
-    assert lib.mla_output_projection(FAKE, FAKE, FAKE, 2, 9, None) == 4
+    def call(o=FAKE, w=FAKE, out=FAKE, B=2, dtype=1, ws=FAKE, ws_bytes=1 << 20):
+        return lib.mla_output_projection(o, w, out, B, dtype, ws, ws_bytes, None)
+    assert call(o=None) == 1 and call(out=None) == 1
+    assert call(w=MISALIGNED) == 3
+    assert call(B=0) == 2
+    assert call(dtype=9) == 4
+    need = lib.mla_output_projection_workspace_size(2, 1)
+    assert need == 8 * 2 * 7168 * 4                       # eight float32 partial sums per output
+    assert call(ws_bytes=need - 1) == 5 and call(ws=None) == 5
+    assert call(ws=ctypes.c_void_p(0x10010)) == 5          # not 256-aligned
+    assert lib.mla_output_projection_workspace_size(2, 0) == 0     # float32 needs none
+    assert lib.mla_output_projection_workspace_size(0, 1) == 0
     hdr = open(HDR).read()
     assert int(re.search(r"#define MLA_D_MODEL (\d+)", hdr).group(1)) == 7168
 
