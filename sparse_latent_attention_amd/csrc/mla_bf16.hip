@@ -976,13 +976,39 @@ constexpr int kUvChunk = 4;                    // splits whose loads are in flig
 constexpr int kUvLds = kUvRows * 1024;
 
 // Wave w's slice of W_UV[h] (rows d = 32w .. 32w+31) as MFMA A fragments:
-// k-step ks, lane half g takes columns 16ks + 8g .. +7.
-__device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h, bf16x8 (&wa)[32]) {
+// k-step ks, lane half g takes columns 16ks + 8g .. +7.  The slice is read as
+// whole 128-byte lines (load (i, m): rows 8i + lane/8, bytes 128m + 16(lane%8)
+// .. +15) into the wave's own LDS rows (1040-byte stride: the 16-byte fragment
+// reads of 32 rows fall in distinct banks), then read back as fragments.
+// Reading the fragments straight from memory takes 32 bytes from each of 32
+// rows per load instruction, which the memory pipeline serves at about half
+// the rate of whole lines.
+constexpr int kUvWRow = 1040;
+constexpr int kUvWLds = 4 * 32 * kUvWRow;
+__device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h, bf16x8 (&wa)[32],
+                                          unsigned char* stage) {
     const int lane = threadIdx.x & 63;
-    const int d = 32 * wave_id() + (lane & 31);
-    const __bf16* wrow = w_uv + ((size_t)h * kValue + d) * kLatent + 8 * (lane >> 5);
+    const int wave = wave_id();
+    unsigned char* mine = stage + wave * 32 * kUvWRow;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(w_uv + ((size_t)h * kValue + 32 * wave) * kLatent);
+    const int r8 = lane >> 3, b16 = 16 * (lane & 7);
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 16 * ks);
+    for (int part = 0; part < 2; ++part) {
+        u32x4 v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = (16 * part + q) >> 3, m = q & 7;
+            v[q] = *reinterpret_cast<const u32x4*>(src + (size_t)(8 * i + r8) * (kLatent * 2) + 128 * m + b16);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = (16 * part + q) >> 3, m = q & 7;
+            *reinterpret_cast<u32x4*>(mine + (8 * i + r8) * kUvWRow + 128 * m + b16) = v[q];
+        }
+    }
+    const unsigned char* frag = mine + (lane & 31) * kUvWRow + 16 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(frag + 32 * ks);
 }
 
 // Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31.  Every thread of
@@ -1102,10 +1128,11 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, 
                                                   const float* __restrict__ l_part,
                                                   const __bf16* __restrict__ w_uv, int R, int n_split,
                                                   int r_groups, __bf16* __restrict__ out) {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvLds];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvWLds > kUvLds ? kUvWLds : kUvLds];
     const int h = blockIdx.x;
     bf16x8 wa[32];
-    uv_load_w(w_uv, h, wa);
+    uv_load_w(w_uv, h, wa, lds);
+    __syncthreads();                     // every wave has its fragments before the merge staging reuses LDS
     for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups)
         uv_block(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
 }
