@@ -187,16 +187,20 @@ __global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __
 }
 
 // --------------------------------------------------------------------------
-// 2. Selection bitmap [S][words], words = ceil(Tv / 32).  Workgroup = one
-// query: its words are built in LDS (kBmChunk words = 262,144 positions at a
-// time; one pass below that) with LDS atomics, then written out whole, so no
-// separate clear is needed.  A listed position counts iff 0 <= t < Tv and
+// 2. Selection bitmap, word-major: word w (positions 32w .. 32w+31) of query s
+// at bm[w * S + s], so that the 128 words a tile of the attention needs are
+// contiguous (its bitmap loads then take 2 cache lines rather than 128).
+// Workgroup = one query: its words are built in LDS with LDS atomics
+// (kBmChunk words = 262,144 positions at a time; one pass below that), then
+// written to their word rows (neighbouring queries' words meet in L2; a
+// workgroup of 32 queries writing whole rows was slower to build and no
+// faster to read).  A listed position counts iff 0 <= t < Tv and
 // t <= start_pos + s.
 // --------------------------------------------------------------------------
 constexpr int kBmChunk = 8192;
 
-__global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ idx, unsigned* __restrict__ bm, int k,
-                                                    int words, int Tv, int start_pos) {
+__global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ idx, unsigned* __restrict__ bm, int S,
+                                                    int k, int words, int Tv, int start_pos) {
     __shared__ unsigned w[kBmChunk];
     const int s = blockIdx.x;
     const int limit = min(Tv - 1, start_pos + s);
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ 
             if (wi >= 0 && wi < n) atomicOr(&w[wi], 1u << (t & 31));
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < n; i += 256) bm[(size_t)s * words + w0 + i] = w[i];
+        for (int i = threadIdx.x; i < n; i += 256) bm[(size_t)(w0 + i) * S + s] = w[i];
         __syncthreads();
     }
 }
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
     // its 40 (16 key-content, 8 rotary, 16 value) and query qb0 + tid % 128's bitmap word (a
     // query past S reads the last one's; its lanes ignore it).
     auto load_tile = [&](int kt, TileRegs& r) {
-        r.bits = bm[(size_t)min(qb0 + (tid & (kQb - 1)), S - 1) * words + kt];
+        r.bits = bm[(size_t)kt * S + min(qb0 + (tid & (kQb - 1)), S - 1)];
         const int row = tid >> 3, c0 = tid & 7;
         const int t = min(kt * 32 + row, Tv - 1);
         const __bf16* kvrow = up + ((size_t)t * kHeads + h) * (2 * kNope);
@@ -517,7 +521,7 @@ hipError_t launch_explicit_prefill(const void* q_nope, const void* q_pe, const v
                        static_cast<const __bf16*>(w_uv), up, p.Tv, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bitmap_build, dim3((unsigned)S), dim3(256), 0, s, idx, bm, k, p.words, p.Tv, start_pos);
+    hipLaunchKernelGGL(bitmap_build, dim3((unsigned)S), dim3(256), 0, s, idx, bm, S, k, p.words, p.Tv, start_pos);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nqb = (S + kQb - 1) / kQb;
     hipLaunchKernelGGL(explicit_attn_bf16, dim3((unsigned)nqb * kHeads), dim3(256), 0, s,
