@@ -1137,6 +1137,75 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, 
         uv_block(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
 }
 
+// The same merge + W_UV when every row has one split (the prefill chunk's lists
+// fit one): the merged row is the split's mix divided by its weight sum.
+// Each wave's partial rows of the workgroup's next block are loaded while the
+// current block is multiplied (two register sets, the loop taking blocks in
+// pairs), so that a workgroup's blocks overlap instead of each waiting for its
+// loads.  Past R, rows are loaded from row R - 1 and dropped.
+__global__ __launch_bounds__(256, 1) void uv1_bf16(const __bf16* __restrict__ o, const float* __restrict__ l_part,
+                                                   const __bf16* __restrict__ w_uv, int R, int r_groups,
+                                                   __bf16* __restrict__ out) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kUvWLds > kUvLds ? kUvWLds : kUvLds];
+    const int h = blockIdx.x;
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    bf16x8 wa[32];
+    uv_load_w(w_uv, h, wa, lds);
+    __syncthreads();                     // every wave has its fragments before the staging reuses LDS
+    const int blocks = (R + kUvRows - 1) / kUvRows;
+    // rows 32 rb + 8 wave + jj (jj < 8): lane l loads latent columns 8l .. 8l+7 of each, and the
+    // weight sum of row 32 rb + 8 wave + l / 8
+    auto load = [&](int rb, bf16x8 (&v)[8], float& l) {
+        const int r0 = min(rb, blocks - 1) * kUvRows + 8 * wave;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            v[jj] = *reinterpret_cast<const bf16x8*>(o + ((size_t)min(r0 + jj, R - 1) * kHeads + h) * kLatent + 8 * lane);
+        l = l_part[(size_t)min(r0 + (lane >> 3), R - 1) * kHeads + h];
+    };
+    auto process = [&](int rb, const bf16x8 (&v)[8], float l) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), 8 * jj));
+            const int j = 8 * wave + jj;
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = (__bf16)((float)v[jj][e] * w);
+            *reinterpret_cast<bf16x8*>(lds + j * 1024 + (((lane & ~15) | ((lane & 15) ^ lat_swz(j))) << 4)) = b;
+        }
+        barrier_lds();
+        const int j = lane & 31;
+        const int b_base = j * 1024 + ((half ^ lat_swz(j)) << 4);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lds + ((b_base ^ ((ks & 7) << 5)) + (ks >> 3) * 256));
+            acc = mfma32(wa[ks], bv, acc);
+        }
+        const int r = rb * kUvRows + j;
+        if (r < R) {
+            __bf16* dst = out + ((size_t)r * kHeads + h) * kValue + 32 * wave + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<bf16x4*>(dst + 8 * g) = to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+        barrier_only();                  // staging reused by the next block
+    };
+    bf16x8 va[8], vb[8];
+    float la, lb;
+    int rb = blockIdx.y;
+    load(rb, va, la);
+    for (; rb < blocks; rb += 2 * r_groups) {
+        load(rb + r_groups, vb, lb);
+        process(rb, va, la);
+        if (rb + r_groups >= blocks) break;
+        load(rb + 2 * r_groups, va, la);
+        process(rb + r_groups, vb, lb);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
@@ -1162,6 +1231,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start, 
 hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStream_t s) {
     const int blocks = (a.R + 31) / 32;
     const int r_groups = blocks < 8 ? blocks : 8;
+    if (a.n_split == 1) {
+        hipLaunchKernelGGL(uv1_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, static_cast<const __bf16*>(a.o),
+                           a.l_part, static_cast<const __bf16*>(w_uv), a.R, r_groups, static_cast<__bf16*>(out));
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, static_cast<const __bf16*>(a.o),
                        a.m_part, a.l_part, static_cast<const __bf16*>(w_uv), a.R, a.n_split, r_groups,
                        static_cast<__bf16*>(out));
