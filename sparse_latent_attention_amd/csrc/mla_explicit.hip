@@ -23,6 +23,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -385,17 +387,35 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
                 }
             } else {
                 sel_or |= bits;
-                bf16x8 pb[2];
-                float psum = 0.f;
+                // Weights in bf16 pairs (elements i, i+1: positions t, t+1): both
+                // converted at once, then the unselected half zeroed with a byte
+                // mask, and the pair's sum added to l_run by one dot product with
+                // (1, 1), so that l_run adds exactly the weights the mix multiplies.
+                // The masks come from the byte permute's sign-replicating selectors
+                // (8: bit 15 of its second source, 9: bit 31; 10, 11: the same of its
+                // first): sh[b] holds the bits moved up so that position b sits at
+                // bit 15 and position b + 16 at bit 31.
+                unsigned sh[8];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = 8 * (i >> 2) + (i & 3);
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], scale_log2, -m_ref));
-                    const float p = (bits >> t) & 1u ? e : 0.f;
-                    psum += p;
-                    pb[i >> 3][i & 7] = (__bf16)p;
+                for (int b = 0; b < 8; ++b) sh[b] = bits << (15 - ((b & 3) + 8 * (b >> 2)));
+                u32x4v pw[2];
+                float psum = 0.f;
+                const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], scale_log2, -m_ref));
+                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i + 1], scale_log2, -m_ref));
+                    const bf16x2 pe2 = {(__bf16)e0, (__bf16)e1};
+                    // positions t = 8 (i / 4) + i % 4 and t + 1; below 16 they sit at
+                    // bit 15 of sh[b], sh[b + 1], from 16 on at bit 31 of them
+                    const int b = (i & 3) + 4 * ((i >> 2) & 1);
+                    const unsigned sel = i < 8 ? 0x0A0A0808u : 0x0B0B0909u;
+                    const unsigned pm = __builtin_bit_cast(unsigned, pe2) & __builtin_amdgcn_perm(sh[b + 1], sh[b], sel);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pm), ones, psum, false);
+                    pw[i >> 3][(i >> 1) & 3] = pm;
                 }
                 l_run += psum;
+                const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
                 const unsigned char* vb0 = kb + kKBytes + tr_off;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
