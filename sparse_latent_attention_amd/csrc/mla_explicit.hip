@@ -262,6 +262,8 @@ constexpr int kVBytes = 32 * kVRow * 2;
 constexpr int kBitsBytes = kQb * 4;       // each query's bitmap word for the tile
 constexpr int kStage = kKBytes + kVBytes + kBitsBytes;
 constexpr int kStages = 3;
+constexpr int kScAhead = 4;                // score operands read ahead of their MFMA
+constexpr int kMixAhead = 3;               // mix operands read ahead of their MFMA
 constexpr int kOutRow = 136;              // bf16 per staged output row (128 + pad)
 static_assert(kQb * kOutRow * 2 <= kStages * kStage, "output staging fits in the tile stages");
 constexpr float kSumHigh = 18446744073709551616.f;   // 2^64
@@ -375,69 +377,90 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
         constexpr bool kMaxOnly = decltype(max_only)::value;
         constexpr bool kFirstRef = decltype(first_ref)::value;
         f32x16 s_cur;
-        auto finish_tile = [&](int kt) {
-            const unsigned char* kb = lds + (kt % kStages) * kStage;
-            const unsigned word = reinterpret_cast<const unsigned*>(kb + kKBytes + kVBytes)[32 * wave + q];
-            const unsigned bits = (word >> (4 * g)) & qmask;
-            if constexpr (kMaxOnly) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = 8 * (i >> 2) + (i & 3);
-                    m_max = (bits >> t) & 1u ? fmaxf(m_max, s_cur[i] * scale_log2) : m_max;
-                }
-            } else {
-                sel_or |= bits;
-                // Weights in bf16 pairs (elements i, i+1: positions t, t+1): both
-                // converted at once, then the unselected half zeroed with a byte
-                // mask, and the pair's sum added to l_run by one dot product with
-                // (1, 1), so that l_run adds exactly the weights the mix multiplies.
-                // The masks come from the byte permute's sign-replicating selectors
-                // (8: bit 15 of its second source, 9: bit 31; 10, 11: the same of its
-                // first): sh[b] holds the bits moved up so that position b sits at
-                // bit 15 and position b + 16 at bit 31.
-                unsigned sh[8];
-#pragma unroll
-                for (int b = 0; b < 8; ++b) sh[b] = bits << (15 - ((b & 3) + 8 * (b >> 2)));
-                u32x4v pw[2];
-                float psum = 0.f;
-                const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], scale_log2, -m_ref));
-                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i + 1], scale_log2, -m_ref));
-                    const bf16x2 pe2 = {(__bf16)e0, (__bf16)e1};
-                    // positions t = 8 (i / 4) + i % 4 and t + 1; below 16 they sit at
-                    // bit 15 of sh[b], sh[b + 1], from 16 on at bit 31 of them
-                    const int b = (i & 3) + 4 * ((i >> 2) & 1);
-                    const unsigned sel = i < 8 ? 0x0A0A0808u : 0x0B0B0909u;
-                    const unsigned pm = __builtin_bit_cast(unsigned, pe2) & __builtin_amdgcn_perm(sh[b + 1], sh[b], sel);
-                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pm), ones, psum, false);
-                    pw[i >> 3][(i >> 1) & 3] = pm;
-                }
-                l_run += psum;
-                const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
-                const unsigned char* vb0 = kb + kKBytes + tr_off;
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                    for (int vb = 0; vb < 4; ++vb) {
-                        const unsigned char* a0 = vb0 + (16 * kc * kVRow + 32 * vb) * 2;
-                        const bf16x8 a = cat(lds_read_tr(a0), lds_read_tr(a0 + 8 * kVRow * 2));
-                        acc[vb] = mfma(a, pb[kc], acc[vb]);
-                    }
-            }
-        };
-        // Step kt: tile kt+2 from its register set to LDS, that set <- tile kt+4, scores of
-        // tile kt+1, weights and mix of tile kt.  Branch-free, so that the compiler's memory-
-        // counter waits see both register sets in flight: past the last tile the last one is
-        // loaded and staged again into a stage nobody reads, and the scores beyond it are
-        // dropped.
+        // Step kt: tile kt+2 from its register set to LDS, that set <- tile kt+4, then the
+        // scores of tile kt+1 with the weights of tile kt between their MFMAs (one pair of
+        // weights per k-step, so that the exponentials issue while an MFMA runs), then the
+        // mix of tile kt.  Operands are read from LDS several MFMAs ahead.  Branch-free, so
+        // that the compiler's memory-counter waits see both register sets in flight: past
+        // the last tile the last one is loaded and staged again into a stage nobody reads,
+        // and the scores beyond it are dropped.
         auto step = [&](int kt, TileRegs& set) {
             store_tile((kt + 2) % kStages, set);
             load_tile(min(kt + 4, last), set);
             __builtin_amdgcn_sched_barrier(0);           // the loads go out before the MFMAs
-            const f32x16 s_next = scores((kt + 1) % kStages);
-            finish_tile(kt);
+            const unsigned char* kb = lds + (kt % kStages) * kStage;
+            const unsigned word = reinterpret_cast<const unsigned*>(kb + kKBytes + kVBytes)[32 * wave + q];
+            const unsigned bits = (word >> (4 * g)) & qmask;
+            // Weights in bf16 pairs (elements i, i+1: positions t, t+1): both converted at
+            // once, then the unselected half zeroed with a byte mask, and the pair's sum
+            // added to l_run by one dot product with (1, 1), so that l_run adds exactly the
+            // weights the mix multiplies.  The masks come from the byte permute's
+            // sign-replicating selectors (8: bit 15 of its second source, 9: bit 31; 10, 11:
+            // the same of its first): sh[b] holds the bits moved up so that position b sits
+            // at bit 15 and position b + 16 at bit 31.
+            unsigned sh[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) sh[b] = bits << (15 - ((b & 3) + 8 * (b >> 2)));
+            u32x4v pw[2];
+            float psum = 0.f;
+            const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+            auto weights = [&](int i) {                   // elements i, i + 1 (i even)
+                if constexpr (kMaxOnly) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int t = 8 * (i >> 2) + (i & 3) + e;
+                        m_max = (bits >> t) & 1u ? fmaxf(m_max, s_cur[i + e] * scale_log2) : m_max;
+                    }
+                } else {
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i], scale_log2, -m_ref));
+                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[i + 1], scale_log2, -m_ref));
+                    const bf16x2 pe2 = {(__bf16)e0, (__bf16)e1};
+                    // positions t = 8 (i / 4) + i % 4 and t + 1; below 16 they sit at bit 15
+                    // of sh[b], sh[b + 1], from 16 on at bit 31 of them
+                    const int b = (i & 3) + 4 * ((i >> 2) & 1);
+                    const unsigned sel = i < 8 ? 0x0A0A0808u : 0x0B0B0909u;
+                    const unsigned pm =
+                        __builtin_bit_cast(unsigned, pe2) & __builtin_amdgcn_perm(sh[b + 1], sh[b], sel);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pm), ones, psum, false);
+                    pw[i >> 3][(i >> 1) & 3] = pm;
+                }
+            };
+            // scores of tile kt+1: A = K[t][16 ks + 8 g' .. +7] for t = lane % 32
+            const __bf16* krow =
+                reinterpret_cast<const __bf16*>(lds + ((kt + 1) % kStages) * kStage) + q * kKStride + 8 * g;
+            bf16x8 pre[kScAhead];
+#pragma unroll
+            for (int d = 0; d < kScAhead; ++d) pre[d] = *reinterpret_cast<const bf16x8*>(krow + 16 * d);
+            f32x16 s_next = {};
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) {
+                const bf16x8 av = pre[ks % kScAhead];
+                if (ks + kScAhead < 12) pre[ks % kScAhead] = *reinterpret_cast<const bf16x8*>(krow + 16 * (ks + kScAhead));
+                s_next = mfma(av, qf[ks], s_next);
+                if (ks < 8) weights(2 * ks);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (!kMaxOnly) {
+                sel_or |= bits;
+                l_run += psum;
+                const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
+                // mix m = 4 kc + vb: acc[vb] += V^T[32 vb ..][16 kc ..] P^T
+                const unsigned char* vb0 = kb + kKBytes + tr_off;
+                auto vread = [&](int m) {
+                    const unsigned char* a0 = vb0 + (16 * (m >> 2) * kVRow + 32 * (m & 3)) * 2;
+                    return cat(lds_read_tr(a0), lds_read_tr(a0 + 8 * kVRow * 2));
+                };
+                bf16x8 va[kMixAhead];
+#pragma unroll
+                for (int d = 0; d < kMixAhead; ++d) va[d] = vread(d);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const bf16x8 av = va[m % kMixAhead];
+                    if (m + kMixAhead < 8) va[m % kMixAhead] = vread(m + kMixAhead);
+                    acc[m & 3] = mfma(av, pb[m >> 2], acc[m & 3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             s_cur = s_next;
             __syncthreads();                              // stage kt free; stage kt+2 complete
         };
