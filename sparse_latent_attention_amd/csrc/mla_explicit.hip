@@ -254,8 +254,10 @@ __global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ 
 // reference far above every selected score (a query with a selection and a
 // weight sum below 2^-60), where weights would lose range.  Neither happens
 // with scores of moderate spread; the common path has no branch.
-// The scores of tile kt+1 are issued before the weights of tile kt, so the
-// matrix cores work while the vector units do the exponentials.  Tiles pass
+// The weights of tile kt are computed between the score MFMAs of tile kt+1
+// (a pair after each of the first eight), so the matrix cores work while the
+// vector units do the exponentials; the weight sum adds the bf16 weights the
+// mix multiplies.  Tiles pass
 // through three LDS stages (kt: values and bitmap words, kt+1: keys, kt+2:
 // being written) and two register sets (tiles kt+3 and kt+4 in flight).
 // --------------------------------------------------------------------------
