@@ -57,15 +57,14 @@ __device__ __forceinline__ void xcd_tile(int nblk, int& head, int& blk) {
 // operand, latent rows the B operand.  Eight waves; wave w computes
 // positions 64 (w / 2) .. +63 and rows 128 (w % 2) .. +127: 2 x 4 MFMA
 // blocks of 32 x 32, 8 MFMAs against 6 16-byte LDS reads per 16 latent
-// columns.  64 columns at a time (one 128-byte line of every row) are staged
-// in LDS (two stages); each thread's share of a chunk comes from memory two
-// chunks ahead, through two register sets, so a chunk has two chunks' worth
-// of MFMA time to arrive.
+// columns.  32 columns at a time are staged in LDS (two stages); each
+// thread's share of a chunk comes from memory two chunks ahead, through two
+// register sets, so a chunk has two chunks' worth of MFMA time to arrive.
 // --------------------------------------------------------------------------
 constexpr int kUpT = 256;                 // positions per workgroup
 constexpr int kUpThreads = 512;
-constexpr int kUpC = 64;                  // latent columns per stage (one 128-byte line per row)
-constexpr int kUpStride = 72;             // bf16 per staged row (64 + pad): conflict-free 16-byte reads
+constexpr int kUpC = 32;                  // latent columns per stage
+constexpr int kUpStride = 40;             // bf16 per staged row (32 + pad): conflict-free 16-byte reads
 constexpr int kUpWBytes = 256 * kUpStride * 2;
 constexpr int kUpXBytes = kUpT * kUpStride * 2;
 constexpr int kUpStage = kUpWBytes + kUpXBytes;
@@ -84,30 +83,25 @@ __global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __
     xcd_tile(nblk, h, blk);
     const int t0 = blk * kUpT;
 
-    // staging: thread tid moves columns 8 (tid % 8) .. +7 of a chunk (eight threads cover a
-    // row's 128 bytes, one whole line) for weight rows prow and prow + 64 of W_UK and of W_UV
-    // (stacked rows prow, prow + 64, 128 + prow, 192 + prow) and latent rows
-    // t0 + prow + 64 i, i < 4
-    const int prow = tid >> 3, pcol = 8 * (tid & 7);
+    // staging: thread tid moves columns 8 (tid % 4) .. +7 of a chunk for weight rows prow
+    // (W_UK) and 128 + prow (W_UV), and for latent rows t0 + prow and t0 + 128 + prow
+    const int prow = tid >> 2, pcol = 8 * (tid & 3);
     const __bf16* wk = w_uk + ((size_t)h * kNope + prow) * kLatent + pcol;
     const __bf16* wv = w_uv + ((size_t)h * kValue + prow) * kLatent + pcol;
-    const __bf16* xr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xr[i] = kv + (size_t)min(t0 + prow + 64 * i, Tv - 1) * kLatent + pcol;
-    auto gload = [&](int c, u32x4 (&v)[8]) {
+    const __bf16* x0 = kv + (size_t)min(t0 + prow, Tv - 1) * kLatent + pcol;
+    const __bf16* x1 = kv + (size_t)min(t0 + 128 + prow, Tv - 1) * kLatent + pcol;
+    auto gload = [&](int c, u32x4 (&v)[4]) {
         v[0] = *reinterpret_cast<const u32x4*>(wk + c * kUpC);
-        v[1] = *reinterpret_cast<const u32x4*>(wk + 64 * kLatent + c * kUpC);
-        v[2] = *reinterpret_cast<const u32x4*>(wv + c * kUpC);
-        v[3] = *reinterpret_cast<const u32x4*>(wv + 64 * kLatent + c * kUpC);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 + i] = *reinterpret_cast<const u32x4*>(xr[i] + c * kUpC);
+        v[1] = *reinterpret_cast<const u32x4*>(wv + c * kUpC);
+        v[2] = *reinterpret_cast<const u32x4*>(x0 + c * kUpC);
+        v[3] = *reinterpret_cast<const u32x4*>(x1 + c * kUpC);
     };
-    auto sstore = [&](int stage, const u32x4 (&v)[8]) {
+    auto sstore = [&](int stage, const u32x4 (&v)[4]) {
         unsigned char* base = lds + stage * kUpStage + (prow * kUpStride + pcol) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + 64 * i * kUpStride * 2) = v[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + kUpWBytes + 64 * i * kUpStride * 2) = v[4 + i];
+        *reinterpret_cast<u32x4*>(base) = v[0];
+        *reinterpret_cast<u32x4*>(base + 128 * kUpStride * 2) = v[1];
+        *reinterpret_cast<u32x4*>(base + kUpWBytes) = v[2];
+        *reinterpret_cast<u32x4*>(base + kUpWBytes + 128 * kUpStride * 2) = v[3];
     };
 
     f32x16 acc[2][4] = {};
@@ -136,7 +130,7 @@ __global__ __launch_bounds__(kUpThreads, 1) void upproject_bf16(const __bf16* __
     // sets in flight and wait for the older one only.
     // The prologue leaves the sets in the loop's order (chunk 1 in set 1 issued before chunk 2
     // in set 0, and the scheduler kept from mixing the two).
-    u32x4 s0[8], s1[8];
+    u32x4 s0[4], s1[4];
     gload(0, s0);
     sstore(0, s0);
     gload(1, s1);
