@@ -109,14 +109,22 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// Layout of the absorbed queries in the workspace, chosen for the attention
-// waves' score operands: element c (0..575: 512 latent, then 64 rotary) of
-// head h of query row r sits at
-//   ((r*4 + h/32)*36 + c/16)*512 + (h%32)*16 + c%16,
-// so the 16-byte operand loads of one wave and k-step read one contiguous
-// 1 KiB run, and the absorption writes 32-byte runs.
-__device__ __forceinline__ size_t q_off(int r, int h, int c) {
-    return (((size_t)r * 4 + (h >> 5)) * 36 + (c >> 4)) * 512 + (size_t)((h & 31) * 16) + (c & 15);
+// Layout of the absorbed queries in the workspace; element c (0..575: 512
+// latent, then 64 rotary) of head h of query row r sits at
+//   ((r*4 + h/32)*36 + c/16)*512 + (h%32)*16 + c%16     (operand image), or
+//   (r*128 + h)*576 + c                                 (row-major).
+// The operand image suits the attention waves' score operands: the 16-byte
+// operand loads of one wave and k-step read one contiguous 1 KiB run, but the
+// absorption writes it in 32-byte pieces.  Row-major, the absorption writes
+// whole lines and the operand loads read 32 bytes from each of 32 rows.  Few
+// query rows (decode) take the image: there the absorption's stores are a few
+// MB and the attention's prologue waits for its queries.  Many rows (a prefill
+// chunk) take row-major: there the absorbed queries are hundreds of MB written
+// once, and each workgroup's query loads are a small part of its work.
+constexpr int kQRowMajorMinRows = 512;
+__device__ __forceinline__ size_t q_off(int r, int h, int c, bool rowmajor) {
+    return rowmajor ? ((size_t)r * kHeads + h) * kQRow + c
+                    : (((size_t)r * 4 + (h >> 5)) * 36 + (c >> 4)) * 512 + (size_t)((h & 31) * 16) + (c & 15);
 }
 
 // --------------------------------------------------------------------------
@@ -146,6 +154,7 @@ constexpr int kAbsorbLds = kNope * kWRow + 32 * kQcRow + 2 * 32 * kQnRow;
 // One unit = (head h, quarter cq of the 512 latent columns), for query blocks
 // rb_first, rb_first + rb_step, ...; `lds` holds kAbsorbLds bytes.  Every
 // thread of the workgroup calls it.
+template <bool kRowMajor>
 __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
                                             const __bf16* __restrict__ q_pe,
                                             const __bf16* __restrict__ w_uk,
@@ -237,7 +246,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             const int e = tid + 256 * i;
             const int rr = rb * 32 + (e >> 4);
             if (rr < R)
-                *reinterpret_cast<u32x4*>(q_out + q_off(rr, h, cq * 128 + 8 * (e & 15))) =
+                *reinterpret_cast<u32x4*>(q_out + q_off(rr, h, cq * 128 + 8 * (e & 15), kRowMajor)) =
                     *reinterpret_cast<const u32x4*>(obuf + (e >> 4) * kQcRow + 16 * (e & 15));
         }
         if (cq == 0) {
@@ -245,7 +254,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             const int rr = rb * 32 + (tid >> 3);
             const int ch = tid & 7;
             if (rr < R) {
-                *reinterpret_cast<bf16x8*>(q_out + q_off(rr, h, kLatent + 8 * ch)) =
+                *reinterpret_cast<bf16x8*>(q_out + q_off(rr, h, kLatent + 8 * ch, kRowMajor)) =
                     *reinterpret_cast<const bf16x8*>(q_pe + ((size_t)rr * kHeads + h) * kRope + 8 * ch);
             }
         }
@@ -275,6 +284,8 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
     }
 }
 
+// kRowMajor: write the absorbed queries row-major (R >= kQRowMajorMinRows), else the operand image.
+template <bool kRowMajor>
 __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ q_nope,
                                                      const __bf16* __restrict__ q_pe,
                                                      const __bf16* __restrict__ w_uk,
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(256) void absorb_q_bf16(const __bf16* __restrict__ 
     // and the 32-byte output pieces of neighbouring heads, which share cache
     // lines, are merged in one L2 before they are written back.
     const int b = blockIdx.x, j = b >> 3;
-    absorb_unit(q_nope, q_pe, w_uk, q_out, R, (16 * (b & 7) + (j >> 2)) * 4 + (j & 3), blockIdx.y,
+    absorb_unit<kRowMajor>(q_nope, q_pe, w_uk, q_out, R, (16 * (b & 7) + (j >> 2)) * 4 + (j & 3), blockIdx.y,
                 r_groups, lds);
 }
 
@@ -417,7 +428,7 @@ struct SplitCtx {
     int* sidx;                   // the split's index list in LDS (-1 past its end)
     const int32_t* idx_src;      // the split's index list in global memory
     int nslots;                  // its length
-    const __bf16* qrow;          // this lane's score operands: k-step ks at qrow + 512*ks
+    const __bf16* qrow;          // this lane's score operands: k-step ks at qrow + 512*ks (image) or 16*ks
     u32x4 kv_desc, pe_desc;
     int r, split, ntiles, limit, T, wave, lane;
 };
@@ -460,7 +471,7 @@ constexpr float kRerunSum = 18446744073709551616.f;   // 2^64
 // passed kRerunSum (the pass's result is then to be discarded).
 // kMaxOnly: the same tile pipeline with no exponentials and no mix; on
 // return m_ref holds each head's largest scaled score over the selected rows.
-template <bool kMaxOnly>
+template <bool kMaxOnly, bool kRowMajor>
 __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x16 (&acc)[16],
                                           float& l_run, bool& beaten, bool preset) {
     const int lane = c.lane;
@@ -482,7 +493,7 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     }
     bf16x8 qf[36];
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + 512 * ks);
+    for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(c.qrow + (kRowMajor ? 16 : 512) * ks);
     // The split's last selected slot: tiles past it hold no selected row (a
     // causal prefill query early in its chunk leaves most of its list empty)
     // and are not processed.
@@ -895,6 +906,7 @@ struct AttnEarly {
 // in turn; the splits of one query row share an XCD, so its absorbed query is
 // read from HBM once.  Latest query rows (most work) go first.  Returns false
 // for a slot past the last row.
+template <bool kRowMajor>
 __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, const AttnEarly& a, int id,
                                            unsigned char* tiles, int* sidx) {
     const int split = (id >> 3) % a.n_split;
@@ -916,7 +928,7 @@ __device__ __forceinline__ bool attn_setup(SplitCtx& c, const AttnArgs& args, co
                              (unsigned)c.T * (kLatent * 2));
     c.pe_desc = make_desc(reinterpret_cast<const __bf16*>(a.pe) + (size_t)c.r * a.cache_rows_per_query * kRope,
                           (unsigned)c.T * (kRope * 2));
-    c.qrow = reinterpret_cast<const __bf16*>(a.q) + q_off(c.r, 32 * c.wave + (c.lane & 31), 8 * (c.lane >> 5));
+    c.qrow = reinterpret_cast<const __bf16*>(a.q) + q_off(c.r, 32 * c.wave + (c.lane & 31), 8 * (c.lane >> 5), kRowMajor);
     c.idx_src = a.idx + (size_t)c.r * a.k + slot_begin;
     c.nslots = nslots;
     return true;
@@ -928,6 +940,8 @@ constexpr int kAttnTilesLds = kBufs * kBufBytes;
 constexpr int kAttnLds = kAttnTilesLds + kMaxSlotsPerSplit * 4 + 8 * 4;   // + per wave: last selected slot, rerun flag
 static_assert(kAttnLds <= 160 * 1024, "attention LDS exceeds a compute unit's 160 KiB");
 
+// kRowMajor: the absorbed queries are row-major (R >= kQRowMajorMinRows), else the operand image.
+template <bool kRowMajor>
 __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* pe, const int32_t* idx,
                                                     const void* q, int R, int T, int k, int n_split,
                                                     int slots_per_split, int causal_base,
@@ -935,12 +949,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttnLds];
     SplitCtx c;
     const AttnEarly early{kv, pe, idx, q, R, T, k, n_split, slots_per_split, causal_base, cache_rows_per_query};
-    if (!attn_setup(c, a, early, blockIdx.x, lds, reinterpret_cast<int*>(lds + kAttnTilesLds)))
+    if (!attn_setup<kRowMajor>(c, a, early, blockIdx.x, lds, reinterpret_cast<int*>(lds + kAttnTilesLds)))
         return;
     f32x16 acc[16];
     float m_ref = -INFINITY, l_run = 0.f;
     bool beaten;
-    attn_pass<false>(c, m_ref, acc, l_run, beaten, false);
+    attn_pass<false, kRowMajor>(c, m_ref, acc, l_run, beaten, false);
     // A split in which a later score beat its head's reference by about 60
     // (log2 units) runs again, by every wave: a pass that finds each head's
     // largest score, then the full pass with it as the reference (never the
@@ -950,9 +964,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* 
     if ((threadIdx.x & 63) == 0) any_beaten[c.wave] = wave_beaten;
     barrier_lds();                       // also: every wave is done with the tiles
     if (any_beaten[0] | any_beaten[1] | any_beaten[2] | any_beaten[3]) {
-        attn_pass<true>(c, m_ref, acc, l_run, beaten, true);
+        attn_pass<true, kRowMajor>(c, m_ref, acc, l_run, beaten, true);
         barrier_lds();                   // every wave is done with the tiles
-        attn_pass<false>(c, m_ref, acc, l_run, beaten, true);
+        attn_pass<false, kRowMajor>(c, m_ref, acc, l_run, beaten, true);
         if (threadIdx.x == 0) atomicAdd(a.stats, 1);
     }
     attn_finish(c, acc, m_ref, l_run);
@@ -1214,7 +1228,8 @@ hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* 
     // weight is read once per eight blocks
     const int blocks = (R + 31) / 32;
     const int r_groups = (blocks + 7) / 8;
-    hipLaunchKernelGGL(absorb_q_bf16, dim3(kHeads * 4, r_groups), dim3(256), 0, s,
+    auto kernel = R >= kQRowMajorMinRows ? absorb_q_bf16<true> : absorb_q_bf16<false>;
+    hipLaunchKernelGGL(kernel, dim3(kHeads * 4, r_groups), dim3(256), 0, s,
                        static_cast<const __bf16*>(q_nope), static_cast<const __bf16*>(q_pe),
                        static_cast<const __bf16*>(w_uk), static_cast<__bf16*>(q_out), R, r_groups, stats);
     return hipGetLastError();
@@ -1222,7 +1237,8 @@ hipError_t launch_absorb_bf16(const void* q_nope, const void* q_pe, const void* 
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int row_groups = (a.R + 7) / 8;
-    hipExtLaunchKernelGGL(attn_bf16, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, start, stop, 0,
+    auto kernel = a.R >= kQRowMajorMinRows ? attn_bf16<true> : attn_bf16<false>;
+    hipExtLaunchKernelGGL(kernel, dim3(row_groups * 8 * a.n_split), dim3(256), 0, s, start, stop, 0,
                           a.kv, a.pe, a.idx, a.q, a.R, a.T, a.k, a.n_split, a.slots_per_split, a.causal_base,
                           a.cache_rows_per_query, a);
     return hipGetLastError();

@@ -149,6 +149,25 @@ def test_prefill_from_position_zero_all_rows(mla):
     assert err <= TOL["bf16"]
 
 
+def test_many_rows_take_row_major_queries(mla):
+    """513 query rows: at 512 rows and more the absorbed queries are stored row-major
+    (whole-line writes) instead of in the operand image; a strided sample of rows that
+    covers every workgroup slot pattern, plus the last rows."""
+    cfg = DecodeConfig(14, "many_rows", B=513, T=200, k=32, dtype="bf16")
+    rows = sorted(set(range(0, cfg.B, 13)) | set(range(cfg.B - 9, cfg.B)))
+    check_decode(mla, cfg, rows=rows)
+
+
+def test_prefill_many_queries_all_rows(mla):
+    """A 600-query chunk (row-major absorbed queries), compared on every query."""
+    cfg = PrefillConfig(15, "prefill_600", S=600, T=700, k=64, start_pos=100, dtype="bf16")
+    inp = synth.prefill_inputs(cfg)
+    out = to_host64(run_prefill(mla, upload(inp), cfg.start_pos))
+    err = rel_err(out, oracle.prefill(inp, start_pos=cfg.start_pos))
+    log(f"prefill 600 queries: rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ edge cases
 
 def _bf16_decode_workspace(rows, k, n_split):
