@@ -343,6 +343,121 @@ def bench_prefill(args, torch, synth, mla, explicit=False):
                      "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None}}), flush=True)
 
 
+def bench_project(args, torch, synth, mla):
+    """The output projection Delta = o W_O at the decode batch (B=64): a weight-streaming product
+    whose algorithmic bytes are the 235 MB bf16 weight plus the head outputs and the result (the
+    14.7 MB of float32 partial sums the kernels exchange are not algorithmic)."""
+    dev = torch.device("cuda:0")
+    B = 64
+    inp = synth.projection_inputs(B, "bf16")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    o, w = up(inp["o"]), up(inp["w_o"])
+    out = torch.empty((B, 7168), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.output_projection_workspace_size(B, torch.bfloat16), dtype=torch.uint8, device=dev)
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    for _ in range(warm):
+        mla.output_projection(o, w, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mla.output_projection(o, w, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = 7168 * 16384 * 2 + B * 16384 * 2 + B * 7168 * 2
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "output projection weight-stream rate (B=64, 7168 x 16384 bf16)", "value": gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic projection_inputs",
+        "config": {"workload": "output projection o [64, 16384] . W_O [7168, 16384]^T, bf16", "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
+def bench_append(args, torch, synth, mla):
+    """The cache append of 4096-position prefill chunks of 8 sequences (B = 8, S = 4096 into 4096-row caches):
+    per position 576 down-projection outputs read and 576 cache values written, bf16.  The
+    one-position decode append of 64 sequences is timed beside it (a latency figure)."""
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float32:
+            return torch.from_numpy(x).to(dev)
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed(cfg, steps, warm):
+        d = {name: up(v) for name, v in synth.append_inputs(cfg).items()}
+
+        def call():
+            mla.cache_append(d["kv_a_out"], d["norm_weight"], d["cos_sin"], d["kv_cache"], d["pe_cache"],
+                             start_pos=cfg.start_pos)
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps
+
+    from synth.generators import AppendConfig
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    sec = timed(AppendConfig(80, "append_chunk", B=8, S=4096, T=4096, start_pos=0, dtype="bf16"), steps, warm)
+    sec_dec = timed(AppendConfig(81, "append_decode", B=64, S=1, T=64, start_pos=63, dtype="bf16"),
+                    steps, warm)
+    nbytes = 8 * 4096 * (576 + 576) * 2 + 512 * 2 + 4096 * 32 * 2 * 4
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "cache append rate (B=8 x S=4096 positions, bf16)", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic append_inputs",
+        "config": {"workload": "cache append: RMSNorm of 512 latent values, rotation of 64 rotary values, "
+                               "write at start_pos; B=8, S=4096, ld_T=4096, bf16", "bytes": nbytes},
+        "decode_append_b64_ms": sec_dec * 1e3,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
+def bench_dequant(args, torch, synth, mla):
+    """The FP8 wkv_b dequantisation: 16.8 MB of E4M3 codes and 4 KB of block scales read,
+    W_UK and W_UV (33.5 MB of bf16) written."""
+    dev = torch.device("cuda:0")
+    d = synth.fp8_wkv_b_inputs()
+    codes = torch.from_numpy(d["codes"]).to(dev)
+    scales = torch.from_numpy(d["scales"]).to(dev)
+    w_uk = torch.empty((128, 128, 512), dtype=torch.bfloat16, device=dev)
+    w_uv = torch.empty_like(w_uk)
+    steps, warm = min(args.steps, 200), min(args.warmup, 50)
+    for _ in range(warm):
+        mla.wkv_b_dequant(codes, scales, w_uk=w_uk, w_uv=w_uv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mla.wkv_b_dequant(codes, scales, w_uk=w_uk, w_uv=w_uv)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = codes.numel() + scales.numel() * 4 + 2 * w_uk.numel() * 2
+    gbs = nbytes / sec / 1e9
+    print(json.dumps({
+        "metric": "FP8 wkv_b dequantisation rate (32768 x 512 E4M3, 128 x 128 block scales)", "value": gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "dtype": "fp8->bf16", "data": "synthetic fp8_wkv_b_inputs",
+        "config": {"workload": "wkv_b dequantisation: E4M3 codes [32768, 512] x block scales -> "
+                               "W_UK, W_UV [128, 128, 512] bf16", "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:

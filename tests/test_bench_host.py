@@ -89,3 +89,12 @@ def test_step_bytes_and_flops():
     # q_nope + q_pe in and the output out (320 bf16 per row and head), 4-byte indices
     assert bench.step_bytes(64, 2048) == 150_994_944 + 33_554_432 + 5_242_880 + 524_288
     assert bench.step_flops(64, 2048) == 131_072 * 2 * 128 * 1088 + 4 * 64 * 128 * 128 * 512
+
+
+def test_every_benchmark_mode_has_its_function():
+    # each mode flag dispatches to a function of the module; a missing one fails only at run time
+    for name in ("bench_prefill", "prefill_measure", "bench_project", "bench_append", "bench_dequant",
+                 "cpu_baseline", "write_traffic", "traffic_from_profile"):
+        assert callable(getattr(bench, name, None)), name
+    args = bench.parse.__code__.co_consts
+    assert any("--no-prefill-extras" in str(c) for c in args) or "--no-prefill-extras" in open(bench.__file__).read()
