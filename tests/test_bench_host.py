@@ -96,5 +96,3 @@ def test_every_benchmark_mode_has_its_function():
     for name in ("bench_prefill", "prefill_measure", "bench_project", "bench_append", "bench_dequant",
                  "cpu_baseline", "write_traffic", "traffic_from_profile"):
         assert callable(getattr(bench, name, None)), name
-    args = bench.parse.__code__.co_consts
-    assert any("--no-prefill-extras" in str(c) for c in args) or "--no-prefill-extras" in open(bench.__file__).read()
