@@ -21,9 +21,9 @@ def mla():
     return m
 
 
-@pytest.mark.parametrize("B,dtype", [(64, "bf16"), (3, "bf16"), (97, "bf16"), (2, "f32")])
+@pytest.mark.parametrize("B,dtype", [(64, "bf16"), (1, "bf16"), (3, "bf16"), (97, "bf16"), (2, "f32")])
 def test_output_projection(mla, B, dtype):
-    # 64 rows: the decode batch (two 32-row blocks, one pass over the weight); 3 and 97:
+    # 64 rows: the decode batch (two 32-row blocks, one pass over the weight); 1, 3 and 97:
     # ragged blocks and a second pass; float32: the plain path
     inp = synth.projection_inputs(B, dtype)
     dev = {k: to_dev(v) for k, v in inp.items()}
