@@ -77,17 +77,10 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Buffer resource over `bytes` bytes at `base`.  A raw buffer load whose
-// offset is >= bytes returns zeros without touching memory; kOutOfRange is
-// such an offset for every buffer these kernels build (<= 2 GiB).
+// A raw buffer load whose offset is >= its descriptor's size returns zeros
+// without touching memory; kOutOfRange is such an offset for every buffer
+// these kernels describe (<= 2 GiB; see make_desc).
 constexpr unsigned kOutOfRange = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 // Combine the values of lanes l and l ^ 32 (v_permlane32_swap exchanges the
 // upper half of one register with the lower half of the other: swapping a
