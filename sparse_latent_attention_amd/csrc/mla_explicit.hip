@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) void bitmap_build(const int32_t* __restrict__ 
 // weight sum below 2^-60), where weights would lose range.  Neither happens
 // with scores of moderate spread; the common path has no branch.
 // The weights of tile kt are computed between the score MFMAs of tile kt+1
-// (a pair after each of the first eight), so the matrix cores work while the
+// (a pair after each of k-steps 2..9), so the matrix cores work while the
 // vector units do the exponentials; the weight sum adds the bf16 weights the
 // mix multiplies.  Tiles pass
 // through three LDS stages (kt: values and bitmap words, kt+1: keys, kt+2:
@@ -381,7 +381,8 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
         f32x16 s_cur;
         // Step kt: tile kt+2 from its register set to LDS, that set <- tile kt+4, then the
         // scores of tile kt+1 with the weights of tile kt between their MFMAs (one pair of
-        // weights per k-step, so that the exponentials issue while an MFMA runs), then the
+        // weights after each of k-steps 2..9, so that the exponentials issue while an MFMA
+        // runs, once the chain's first operand reads are under way), then the
         // mix of tile kt.  Operands are read from LDS several MFMAs ahead.  Branch-free, so
         // that the compiler's memory-counter waits see both register sets in flight: past
         // the last tile the last one is loaded and staged again into a stage nobody reads,
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
                 const bf16x8 av = pre[ks % kScAhead];
                 if (ks + kScAhead < 12) pre[ks % kScAhead] = *reinterpret_cast<const bf16x8*>(krow + 16 * (ks + kScAhead));
                 s_next = mfma(av, qf[ks], s_next);
-                if (ks < 8) weights(2 * ks);
+                if (ks >= 2 && ks < 10) weights(2 * (ks - 2));
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
