@@ -265,7 +265,6 @@ constexpr int kBitsBytes = kQb * 4;       // each query's bitmap word for the ti
 constexpr int kStage = kKBytes + kVBytes + kBitsBytes;
 constexpr int kStages = 3;
 constexpr int kScAhead = 4;                // score operands read ahead of their MFMA
-constexpr int kMixAhead = 3;               // mix operands read ahead of their MFMA
 constexpr int kOutRow = 136;              // bf16 per staged output row (128 + pad)
 static_assert(kQb * kOutRow * 2 <= kStages * kStage, "output staging fits in the tile stages");
 constexpr float kSumHigh = 18446744073709551616.f;   // 2^64
@@ -382,8 +381,10 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
         // Step kt: tile kt+2 from its register set to LDS, that set <- tile kt+4, then the
         // scores of tile kt+1 with the weights of tile kt between their MFMAs (one pair of
         // weights after each of k-steps 2..9, so that the exponentials issue while an MFMA
-        // runs, once the chain's first operand reads are under way), then the
-        // mix of tile kt.  Operands are read from LDS several MFMAs ahead.  Branch-free, so
+        // runs, once the chain's first operand reads are under way) and the mix of tile kt
+        // between them too, as soon as its weights are complete: its MFMAs are independent of
+        // the chain's and fill the chain's dependency gaps.  Operands are read from LDS
+        // several MFMAs ahead.  Branch-free, so
         // that the compiler's memory-counter waits see both register sets in flight: past
         // the last tile the last one is loaded and staged again into a stage nobody reads,
         // and the scores beyond it are dropped.
@@ -435,9 +436,20 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
 #pragma unroll
             for (int d = 0; d < kScAhead; ++d) pre[d] = *reinterpret_cast<const bf16x8*>(krow + 16 * d);
             f32x16 s_next = {};
-            // Raised wave priority for the score chain and the weights between its MFMAs: with
-            // two workgroups per CU each SIMD runs two waves, and the one in this phase then
-            // issues ahead of one storing tiles, mixing or waiting at the barrier (6% faster).
+            // mix m = 4 kc + vb: acc[vb] += V^T[32 vb ..][16 kc ..] P^T, interleaved with the
+            // chain: the weights of elements 0..7 (pb[0]) are done after k-step 5, those of
+            // 8..15 after k-step 9; mix MFMAs m = 0..3 follow k-steps 6..9 and m = 4..7 two each
+            // follow k-steps 10 and 11, in the gaps of the chain's dependent MFMAs.  Each
+            // accumulator still takes its two MFMAs in the order kc = 0, 1.
+            const unsigned char* vb0 = kb + kKBytes + tr_off;
+            auto vread = [&](int m) {
+                const unsigned char* a0 = vb0 + (16 * (m >> 2) * kVRow + 32 * (m & 3)) * 2;
+                return cat(lds_read_tr(a0), lds_read_tr(a0 + 8 * kVRow * 2));
+            };
+            bf16x8 va[8];
+            // Raised wave priority for this phase: with two workgroups per CU each SIMD runs two
+            // waves, and the one in its score chain then issues ahead of one storing a tile or
+            // waiting at the barrier.
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < 12; ++ks) {
@@ -445,29 +457,31 @@ __global__ __launch_bounds__(256, 2) void explicit_attn_bf16(const __bf16* __res
                 if (ks + kScAhead < 12) pre[ks % kScAhead] = *reinterpret_cast<const bf16x8*>(krow + 16 * (ks + kScAhead));
                 s_next = mfma(av, qf[ks], s_next);
                 if (ks >= 2 && ks < 10) weights(2 * (ks - 2));
+                if constexpr (!kMaxOnly) {
+                    // mix operands: m = 0..3 read at k-steps 3..6, m = 4..7 at 7..10
+                    if (ks >= 3 && ks < 11) va[ks - 3] = vread(ks - 3);
+                    // mix MFMAs: m = 0..3 after k-steps 6..9 (pb[0] complete after k-step 5),
+                    // m = 4..7 after k-steps 10, 10, 11, 11 (pb[1] complete after k-step 9)
+                    if (ks >= 6 && ks < 10) {
+                        const int m = ks - 6;
+                        const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pw[0]);
+                        acc[m] = mfma(va[m], pb0, acc[m]);
+                    }
+                    if (ks >= 10) {
+                        const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pw[1]);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int m = 4 + 2 * (ks - 10) + u;
+                            acc[m & 3] = mfma(va[m], pb1, acc[m & 3]);
+                        }
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
             if constexpr (!kMaxOnly) {
                 sel_or |= bits;
                 l_run += psum;
-                const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
-                // mix m = 4 kc + vb: acc[vb] += V^T[32 vb ..][16 kc ..] P^T
-                const unsigned char* vb0 = kb + kKBytes + tr_off;
-                auto vread = [&](int m) {
-                    const unsigned char* a0 = vb0 + (16 * (m >> 2) * kVRow + 32 * (m & 3)) * 2;
-                    return cat(lds_read_tr(a0), lds_read_tr(a0 + 8 * kVRow * 2));
-                };
-                bf16x8 va[kMixAhead];
-#pragma unroll
-                for (int d = 0; d < kMixAhead; ++d) va[d] = vread(d);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const bf16x8 av = va[m % kMixAhead];
-                    if (m + kMixAhead < 8) va[m % kMixAhead] = vread(m + kMixAhead);
-                    acc[m & 3] = mfma(av, pb[m >> 2], acc[m & 3]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
             s_cur = s_next;
             __syncthreads();                              // stage kt free; stage kt+2 complete
