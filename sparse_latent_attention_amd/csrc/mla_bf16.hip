@@ -857,21 +857,29 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     barrier_only();                                      // every wave is done with the tiles
 
     // acc[cb] element i: head h_own, column 32*cb + 8*(i/4) + 4*(lane/32) + i%4.
+    // A quarter of the columns at a time: the stores of one quarter drain
+    // while the next is staged.
     unsigned char* mine = c.tiles + h_own * kOutRow + 8 * (lane >> 5);
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const f32x16& v = acc[cb];
-            *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
-                to_bf16x4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
-        }
     __bf16* dst0 = reinterpret_cast<__bf16*>(a.o) + (((size_t)c.split * a.R + c.r) * kHeads + 32 * c.wave) * kLatent;
     const unsigned char* stage = c.tiles + 32 * c.wave * kOutRow;
-#pragma unroll 8
-    for (int row = 0; row < 32; ++row) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOutRow + 16 * lane);
-        *reinterpret_cast<u32x4*>(dst0 + (size_t)row * kLatent + 8 * lane) = v;
+#pragma unroll
+    for (int qc = 0; qc < 4; ++qc) {
+#pragma unroll
+        for (int cb = 4 * qc; cb < 4 * qc + 4; ++cb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x16& v = acc[cb];
+                *reinterpret_cast<bf16x4*>(mine + 64 * cb + 16 * gq) =
+                    to_bf16x4(v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]);
+            }
+        // 32 head rows x 256 bytes: lane l takes row 4s + l/16, bytes 16(l%16) .. +15 of the quarter
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = 4 * s + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOutRow + 256 * qc + 16 * (lane & 15));
+            *reinterpret_cast<u32x4*>(dst0 + (size_t)row * kLatent + 128 * qc + 8 * (lane & 15)) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (lane < 32) {
         const size_t orow = ((size_t)c.split * a.R + c.r) * kHeads + h_own;
