@@ -165,17 +165,23 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
 
     // One 32-row query block: thread t fetches 32 bytes, row t/8, columns
     // d = 16*(t%8) .. +15 (rows past R read as zeros), and stages them in LDS.
-    auto load_q = [&](int rb, u32x4 (&p)[2]) {
+    // The column quarter cq = 0 also copies the block's q_pe rows (thread t:
+    // row t/8, 16-byte chunk t%8), loaded here with the block so that the copy
+    // adds no memory round trip after the multiply.
+    auto load_q = [&](int rb, u32x4 (&p)[3]) {
         const int r = rb * 32 + (tid >> 3);
         const bool rv = r < R;
         const __bf16* qn = q_nope + ((size_t)(rv ? r : 0) * kHeads + h) * kNope + 16 * (tid & 7);
         p[0] = rv ? *reinterpret_cast<const u32x4*>(qn) : u32x4{};
         p[1] = rv ? *reinterpret_cast<const u32x4*>(qn + 8) : u32x4{};
+        p[2] = rv && cq == 0 ? *reinterpret_cast<const u32x4*>(q_pe + ((size_t)r * kHeads + h) * kRope + 8 * (tid & 7))
+                             : u32x4{};
     };
-    auto stage_q = [&](const u32x4 (&p)[2], unsigned char* qb) {
+    auto stage_q = [&](const u32x4 (&p)[3], unsigned char* qb, u32x4& pe) {
         unsigned char* dst = qb + (tid >> 3) * kQnRow + 32 * (tid & 7);
         *reinterpret_cast<u32x4*>(dst) = p[0];
         *reinterpret_cast<u32x4*>(dst + 16) = p[1];
+        pe = p[2];
     };
     // B fragments of a staged block: q_nope[r][h][16ks + 8half .. +7], r = lane % 32
     auto frags_q = [&](const unsigned char* qb, bf16x8 (&b)[8]) {
@@ -185,7 +191,8 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
     };
     const int blocks = (R + 31) / 32;
     bf16x8 b0[8], b1[8];
-    u32x4 p0[2], p1[2];
+    u32x4 p0[3], p1[3];
+    u32x4 pe0 = {}, pe1 = {};          // q_pe chunks of the blocks in b0 and b1
     load_q(rb_first, p0);
     if (rb_first + r_groups < blocks) load_q(rb_first + r_groups, p1);
 
@@ -204,8 +211,8 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             *reinterpret_cast<u32x4*>(wbuf + (e >> 4) * kWRow + 16 * (e & 15)) = v[i];
         }
     }
-    stage_q(p0, qbuf[0]);
-    if (rb_first + r_groups < blocks) stage_q(p1, qbuf[1]);
+    stage_q(p0, qbuf[0], pe0);
+    if (rb_first + r_groups < blocks) stage_q(p1, qbuf[1], pe1);
     __syncthreads();
     frags_q(qbuf[0], b0);
     if (rb_first + r_groups < blocks) frags_q(qbuf[1], b1);
@@ -222,7 +229,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             a[ks] = cat(lds_read_tr(base + 16 * ks * kWRow), lds_read_tr(base + (16 * ks + 4) * kWRow));
     }
 
-    auto process = [&](int rb, const bf16x8 (&b)[8]) {
+    auto process = [&](int rb, const bf16x8 (&b)[8], const u32x4& pe) {
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], b[ks], acc);
@@ -245,11 +252,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
         if (cq == 0) {
             // q_pe rows of this block: 32 rows x 8 chunks of 16 bytes = one per thread.
             const int rr = rb * 32 + (tid >> 3);
-            const int ch = tid & 7;
-            if (rr < R) {
-                *reinterpret_cast<bf16x8*>(q_out + q_off(rr, h, kLatent + 8 * ch, kRowMajor)) =
-                    *reinterpret_cast<const bf16x8*>(q_pe + ((size_t)rr * kHeads + h) * kRope + 8 * ch);
-            }
+            if (rr < R) *reinterpret_cast<u32x4*>(q_out + q_off(rr, h, kLatent + 8 * (tid & 7), kRowMajor)) = pe;
         }
         __syncthreads();                  // obuf reused by the next block
     };
@@ -262,12 +265,12 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
         const bool has1 = rb + r_groups < blocks;
         const bool more1 = rb + 3 * r_groups < blocks;
         if (more0) load_q(rb + 2 * r_groups, p0);
-        process(rb, b0);
-        if (more0) stage_q(p0, qbuf[0]);
+        process(rb, b0, pe0);
+        if (more0) stage_q(p0, qbuf[0], pe0);
         if (has1) {
             if (more1) load_q(rb + 3 * r_groups, p1);
-            process(rb + r_groups, b1);
-            if (more1) stage_q(p1, qbuf[1]);
+            process(rb + r_groups, b1, pe1);
+            if (more1) stage_q(p1, qbuf[1], pe1);
         }
         if (more0) {
             __syncthreads();              // staged blocks visible
