@@ -1066,9 +1066,15 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
     const bool wrow = wj < nr;
     const size_t wrow_off = (size_t)(r0 + (wrow ? wj : 0)) * kHeads + h;
     float mrow = -INFINITY, lrow = 0.f;
+    // (sum, reference) of split wu, kept for the first chunk's weights below
+    float l_first = 0.f, m_first = -INFINITY;
     for (int sp = wu; sp < n_split; sp += 8) {
         const float l = wrow ? l_part[sp * split_stride + wrow_off] : 0.f;
         const float m = wrow ? m_part[sp * split_stride + wrow_off] : -INFINITY;
+        if (sp == wu) {
+            l_first = l;
+            m_first = m;
+        }
         if (l > 0.f) {
             const float mn = fmaxf(mrow, m);
             lrow = lrow * exp2f(mrow - mn) + l * exp2f(m - mn);
@@ -1092,11 +1098,17 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
         for (int e = 0; e < 8; ++e) x[jj][e] = 0.f;
     for (int s0 = 0;;) {
         // weight of split s0 + (l % 8) for row l / 8 (lanes with l % 8 >= kUvChunk idle)
+        // (the first chunk's pairs are the ones read above; later chunks read
+        // theirs, both values at once)
         float w = 0.f;
         if (wrow && wu < kUvChunk && s0 + wu < n_split) {
-            const size_t o = (size_t)(s0 + wu) * split_stride + wrow_off;
-            const float l = l_part[o];
-            w = l > 0.f ? exp2f(m_part[o] - mrow) * inv_row : 0.f;
+            float l = l_first, m = m_first;
+            if (s0 > 0) {
+                const size_t o = (size_t)(s0 + wu) * split_stride + wrow_off;
+                l = l_part[o];
+                m = m_part[o];
+            }
+            w = l > 0.f ? exp2f(m - mrow) * inv_row : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < kUvChunk; ++u)
