@@ -1031,6 +1031,8 @@ __device__ __forceinline__ void uv_load_w(const __bf16* __restrict__ w_uv, int h
 
 // Merge + W_UV of head h for query rows 32*rb .. 32*rb + 31.  Every thread of
 // the workgroup calls it; `lds` holds kUvLds bytes (1 KiB aligned).
+// kManySplits: more than eight splits (each lane then combines several pairs).
+template <bool kManySplits>
 __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const float* __restrict__ m_part,
                                          const float* __restrict__ l_part, __bf16* __restrict__ out, int R,
                                          int n_split, int h, int rb, const bf16x8 (&wa)[32],
@@ -1042,43 +1044,57 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
     const int r0 = rb * kUvRows + 8 * wave;                    // this wave's first row
     const int nr = max(0, min(8, R - r0));                     // its rows inside R
 
-    // This wave's partial rows of splits s0 .. s0+kUvChunk-1 (zeros past the
-    // last split or past R), 16 bytes per lane and row: columns 8l .. 8l+7.
+    // Merge weights, computed while the first partial loads are in flight.
+    // Lane l works on row jj = l / 8 of the wave's eight rows and on the
+    // splits s with s % 8 == l % 8; the eight lanes of a row then combine
+    // their (reference, sum) pairs into the row's largest reference M and
+    // the inverse of its total weight sum_s l_s 2^(m_s - M).  Each lane's
+    // first pair (split l % 8, kept for the first chunk's weights below) is
+    // loaded ahead of the partials, from a row and split clamped into range.
+    const int wj = lane >> 3, wu = lane & 7;
+    const bool wrow = wj < nr;
+    const size_t wrow_off = (size_t)(r0 + (wrow ? wj : 0)) * kHeads + h;
+    const size_t o_first = (size_t)min(wu, n_split - 1) * split_stride + (size_t)min(r0 + wj, R - 1) * kHeads + h;
+    const float l_ld = l_part[o_first], m_ld = m_part[o_first];
+
+    // This wave's partial rows of splits s0 .. s0+kUvChunk-1, 16 bytes per
+    // lane and row: columns 8l .. 8l+7.  Every load is issued, from a row the
+    // attention kernel wrote (split and row clamped into range), so that the
+    // count of loads in flight does not depend on the sizes; past the last
+    // split or past R the value carries merge weight 0.
     bf16x8 v[kUvChunk][8];
     auto issue = [&](int s0) {
 #pragma unroll
         for (int u = 0; u < kUvChunk; ++u)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const bool ok = s0 + u < n_split && jj < nr;
-                const __bf16* src = o_ws + ((size_t)(s0 + u) * split_stride + (size_t)(r0 + jj) * kHeads + h) * kLatent;
-                v[u][jj] = ok ? *reinterpret_cast<const bf16x8*>(src + 8 * lane) : bf16x8{};
+                const size_t row = (size_t)min(s0 + u, n_split - 1) * split_stride +
+                                   (size_t)min(r0 + jj, R - 1) * kHeads + h;
+                v[u][jj] = *reinterpret_cast<const bf16x8*>(o_ws + row * kLatent + 8 * lane);
             }
     };
     issue(0);
+    __builtin_amdgcn_sched_barrier(0);   // the partial loads go out before the weights are computed
 
-    // Merge weights, computed while the first partial loads are in flight.
-    // Lane l works on row jj = l / 8 of the wave's eight rows and on the
-    // splits s with s % 8 == l % 8; the eight lanes of a row then combine
-    // their (reference, sum) pairs into the row's largest reference M and
-    // the inverse of its total weight sum_s l_s 2^(m_s - M).
-    const int wj = lane >> 3, wu = lane & 7;
-    const bool wrow = wj < nr;
-    const size_t wrow_off = (size_t)(r0 + (wrow ? wj : 0)) * kHeads + h;
+    const bool first_ok = wrow && wu < n_split;
+    const float l_first = first_ok ? l_ld : 0.f, m_first = first_ok ? m_ld : -INFINITY;
     float mrow = -INFINITY, lrow = 0.f;
-    // (sum, reference) of split wu, kept for the first chunk's weights below
-    float l_first = 0.f, m_first = -INFINITY;
-    for (int sp = wu; sp < n_split; sp += 8) {
-        const float l = wrow ? l_part[sp * split_stride + wrow_off] : 0.f;
-        const float m = wrow ? m_part[sp * split_stride + wrow_off] : -INFINITY;
-        if (sp == wu) {
-            l_first = l;
-            m_first = m;
-        }
-        if (l > 0.f) {
-            const float mn = fmaxf(mrow, m);
-            lrow = lrow * exp2f(mrow - mn) + l * exp2f(m - mn);
-            mrow = mn;
+    if (l_first > 0.f) {
+        mrow = m_first;
+        lrow = l_first;
+    }
+    // (with at most eight splits there is nothing more, and the compiler's
+    // count of loads in flight stays exact: the weights below then need only
+    // the pairs, not the partials)
+    if constexpr (kManySplits) {
+        for (int sp = wu + 8; sp < n_split; sp += 8) {
+            const float l = wrow ? l_part[sp * split_stride + wrow_off] : 0.f;
+            const float m = wrow ? m_part[sp * split_stride + wrow_off] : -INFINITY;
+            if (l > 0.f) {
+                const float mn = fmaxf(mrow, m);
+                lrow = lrow * exp2f(mrow - mn) + l * exp2f(m - mn);
+                mrow = mn;
+            }
         }
     }
 #pragma unroll
@@ -1154,6 +1170,7 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
     barrier_only();                      // staging reused by the next block
 }
 
+template <bool kManySplits>
 __global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, const float* __restrict__ m_part,
                                                   const float* __restrict__ l_part,
                                                   const __bf16* __restrict__ w_uv, int R, int n_split,
@@ -1164,7 +1181,7 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, 
     uv_load_w(w_uv, h, wa, lds);
     __syncthreads();                     // every wave has its fragments before the merge staging reuses LDS
     for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups)
-        uv_block(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
+        uv_block<kManySplits>(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
 }
 
 // The same merge + W_UV when every row has one split (the prefill chunk's lists
@@ -1269,7 +1286,8 @@ hipError_t launch_uv_bf16(const AttnArgs& a, const void* w_uv, void* out, hipStr
                            a.l_part, static_cast<const __bf16*>(w_uv), a.R, r_groups, static_cast<__bf16*>(out));
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(uv_bf16, dim3(kHeads, r_groups), dim3(256), 0, s, static_cast<const __bf16*>(a.o),
+    hipLaunchKernelGGL(a.n_split > 8 ? uv_bf16<true> : uv_bf16<false>, dim3(kHeads, r_groups), dim3(256), 0, s,
+                       static_cast<const __bf16*>(a.o),
                        a.m_part, a.l_part, static_cast<const __bf16*>(w_uv), a.R, a.n_split, r_groups,
                        static_cast<__bf16*>(out));
     return hipGetLastError();
