@@ -857,7 +857,7 @@ __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&ac
     const int lane = c.lane;
     const float l_tot = pair_sum(l_run);                 // a head spans lanes l and l ^ 32
     const int h_own = 32 * c.wave + (lane & 31);
-    barrier_only();                                      // every wave is done with the tiles
+    // (the caller has passed a barrier after every wave is done with the tiles)
 
     // acc[cb] element i: head h_own, column 32*cb + 8*(i/4) + 4*(lane/32) + i%4.
     // A quarter of the columns at a time: the stores of one quarter drain
@@ -972,6 +972,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* 
         barrier_lds();                   // every wave is done with the tiles
         attn_pass<false, kRowMajor>(c, m_ref, acc, l_run, beaten, true);
         if (threadIdx.x == 0) atomicAdd(a.stats, 1);
+        barrier_lds();                   // every wave is done with the tiles
     }
     attn_finish(c, acc, m_ref, l_run);
 }
@@ -1112,20 +1113,15 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
     for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[jj][e] = 0.f;
-    for (int s0 = 0;;) {
-        // weight of split s0 + (l % 8) for row l / 8 (lanes with l % 8 >= kUvChunk idle)
-        // (the first chunk's pairs are the ones read above; later chunks read
-        // theirs, both values at once)
+    // One chunk of kUvChunk splits: the weight of split s0 + (l % 8) for row
+    // l / 8 from its pair (lanes with l % 8 >= kUvChunk idle), broadcast to
+    // the rows' lanes.  The first chunk is straight-line code (its pairs are
+    // the ones read above), so that its multiply-adds wait for each partial
+    // load as it lands; later chunks (more than four splits) read their pairs,
+    // both values at once.
+    auto merge_chunk = [&](int s0, float l, float m) {
         float w = 0.f;
-        if (wrow && wu < kUvChunk && s0 + wu < n_split) {
-            float l = l_first, m = m_first;
-            if (s0 > 0) {
-                const size_t o = (size_t)(s0 + wu) * split_stride + wrow_off;
-                l = l_part[o];
-                m = m_part[o];
-            }
-            w = l > 0.f ? exp2f(m - mrow) * inv_row : 0.f;
-        }
+        if (wrow && wu < kUvChunk && s0 + wu < n_split) w = l > 0.f ? exp2f(m - mrow) * inv_row : 0.f;
 #pragma unroll
         for (int u = 0; u < kUvChunk; ++u)
 #pragma unroll
@@ -1135,9 +1131,12 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[jj][e] = fmaf(wv, (float)v[u][jj][e], x[jj][e]);
             }
-        s0 += kUvChunk;
-        if (s0 >= n_split) break;
+    };
+    merge_chunk(0, l_first, m_first);
+    for (int s0 = kUvChunk; s0 < n_split; s0 += kUvChunk) {
         issue(s0);
+        const size_t o = (size_t)min(s0 + wu, n_split - 1) * split_stride + wrow_off;
+        merge_chunk(s0, l_part[o], m_part[o]);
     }
     // Stage the merged rows (bf16) for the B operand: 16-byte chunk l of row j
     // at chunk (l & ~15) | ((l & 15) ^ lat_swz(j)).
