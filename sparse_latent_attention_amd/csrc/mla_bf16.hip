@@ -229,7 +229,8 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             a[ks] = cat(lds_read_tr(base + 16 * ks * kWRow), lds_read_tr(base + (16 * ks + 4) * kWRow));
     }
 
-    auto process = [&](int rb, const bf16x8 (&b)[8], const u32x4& pe) {
+    // `last`: no later block of this workgroup reuses the staging
+    auto process = [&](int rb, const bf16x8 (&b)[8], const u32x4& pe, bool last) {
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], b[ks], acc);
@@ -254,7 +255,7 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
             const int rr = rb * 32 + (tid >> 3);
             if (rr < R) *reinterpret_cast<u32x4*>(q_out + q_off(rr, h, kLatent + 8 * (tid & 7), kRowMajor)) = pe;
         }
-        __syncthreads();                  // obuf reused by the next block
+        if (!last) __syncthreads();       // obuf reused by the next block
     };
     // Two query blocks in flight: while one is multiplied, the next but one
     // loads; it is staged once every wave has its fragments of the block
@@ -265,11 +266,11 @@ __device__ __forceinline__ void absorb_unit(const __bf16* __restrict__ q_nope,
         const bool has1 = rb + r_groups < blocks;
         const bool more1 = rb + 3 * r_groups < blocks;
         if (more0) load_q(rb + 2 * r_groups, p0);
-        process(rb, b0, pe0);
+        process(rb, b0, pe0, !has1);
         if (more0) stage_q(p0, qbuf[0], pe0);
         if (has1) {
             if (more1) load_q(rb + 3 * r_groups, p1);
-            process(rb + r_groups, b1, pe1);
+            process(rb + r_groups, b1, pe1, !more0);
             if (more1) stage_q(p1, qbuf[1], pe1);
         }
         if (more0) {
@@ -1166,7 +1167,6 @@ __device__ __forceinline__ void uv_block(const __bf16* __restrict__ o_ws, const 
         for (int g = 0; g < 4; ++g)
             *reinterpret_cast<bf16x4*>(dst + 8 * g) = to_bf16x4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
     }
-    barrier_only();                      // staging reused by the next block
 }
 
 template <bool kManySplits>
@@ -1179,8 +1179,10 @@ __global__ __launch_bounds__(256, 1) void uv_bf16(const __bf16* __restrict__ o, 
     bf16x8 wa[32];
     uv_load_w(w_uv, h, wa, lds);
     __syncthreads();                     // every wave has its fragments before the merge staging reuses LDS
-    for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups)
+    for (int rb = blockIdx.y; rb * kUvRows < R; rb += r_groups) {
+        if (rb != (int)blockIdx.y) barrier_only();       // the staging is reused by this block
         uv_block<kManySplits>(o, m_part, l_part, out, R, n_split, h, rb, wa, lds);
+    }
 }
 
 // The same merge + W_UV when every row has one split (the prefill chunk's lists
