@@ -494,14 +494,16 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
     // The split's last selected slot: tiles past it hold no selected row (a
     // causal prefill query early in its chunk leaves most of its list empty)
     // and are not processed.
+    // For this wave (slots threadIdx.x + 256 u): the highest u with a selected
+    // slot in some lane, and there the highest such lane, from one ballot per
+    // u (shuffles would put a chain of LDS round trips before the list's store).
     int last_sel = -1;
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
+    for (int u = kIdxPerThread - 1; u >= 0; --u) {
         const int i = (int)threadIdx.x + 256 * u;
-        if (i < c.nslots && (unsigned)iv[u] < lim) last_sel = i;
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(i < c.nslots && (unsigned)iv[u] < lim);
+        if (last_sel < 0 && m != 0ull) last_sel = 256 * u + 64 * c.wave + (63 - __builtin_clzll(m));
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) last_sel = max(last_sel, __shfl_xor(last_sel, o));
     if (lane == 0) c.sidx[kMaxSlotsPerSplit + c.wave] = last_sel;
 #pragma unroll
     for (int u = 0; u < kIdxPerThread; ++u) {
