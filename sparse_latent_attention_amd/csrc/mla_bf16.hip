@@ -808,25 +808,33 @@ __device__ __forceinline__ void attn_pass(const SplitCtx& c, float& m_ref, f32x1
         mix(t, pb, [](int) {}, [](int) {});
     };
 
-    // The first score chain needs the query fragments and tile 0 only.  The
-    // wait for them is a full one: the compiler does not see the gathers
-    // (inline assembly), so after a partial wait it would still take the
-    // later query loads for pending and wait again inside the first score
-    // chain, on counts that include the gathers of tiles 1 and 2.  Those go
-    // out during that chain, spread over its k-steps rather than back to
-    // back, so that its MFMAs cover their issue.
+    // The first score chain needs the query fragments and tile 0 only.  Tile
+    // 1 is gathered right behind tile 0 (groups under different M0 values go
+    // out a short sleep apart: back to back, each would wait for the one
+    // before it), so that it is in flight while the chain runs; one wait then
+    // leaves only tile 1's nine loads outstanding: the query fragments, which
+    // were loaded first, and tile 0 have landed.  The compiler does not see
+    // the gathers (inline assembly) and takes the last query loads for
+    // pending, so its own waits in the chain's last k-steps also wait for tile
+    // 1, which the loop needs next anyway.  Tile 2 goes out after the chain
+    // (the compiler has no load of its own pending then), ahead of the
+    // hand-over, whose wait then leaves tile 2 in flight as in the loop.
     gather_tile(0);
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_sleep(2);
+    gather_rows4(1, 0);
+    __builtin_amdgcn_s_sleep(2);
+    gather_rows4(1, 1);
+    __builtin_amdgcn_s_sleep(2);
+    gather_pe(1, gather_index(1));
+    MLA_WAIT_VMCNT(9);
     barrier_only();
     f32x16 sA, sB;
-    scores(0, sA, [&](int ks) {
-        if (ks == 2) gather_rows4(1, 0);
-        if (ks == 8) gather_rows4(1, 1);
-        if (ks == 14) gather_pe(1, gather_index(1));
-        if (ks == 20) gather_rows4(2, 0);
-        if (ks == 26) gather_rows4(2, 1);
-        if (ks == 32) gather_pe(2, gather_index(2));
-    });
+    scores(0, sA, [&](int) {});
+    gather_rows4(2, 0);
+    __builtin_amdgcn_s_sleep(2);
+    gather_rows4(2, 1);
+    __builtin_amdgcn_s_sleep(2);
+    gather_pe(2, gather_index(2));
     if (ntiles > 1) hand_over(1);
     read_rows(3);
 #pragma unroll
