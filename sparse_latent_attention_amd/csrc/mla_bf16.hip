@@ -101,6 +101,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
+// This lane's index within its wave, from the execution mask (no register
+// needs to hold it: after a long loop that uses every register, the compiler
+// would otherwise reload a spilled thread index from scratch memory).
+__device__ __forceinline__ int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
 
 // Layout of the absorbed queries in the workspace; element c (0..575: 512
 // latent, then 64 rotary) of head h of query row r sits at
@@ -865,7 +871,7 @@ constexpr int kOutRow = 1040;   // staged output row: 512 bf16 + 16 bytes (sprea
 __device__ __forceinline__ void attn_finish(const SplitCtx& c, const f32x16 (&acc)[16], float m_ref,
                                             float l_run) {
     const AttnArgs& a = *c.a;
-    const int lane = c.lane;
+    const int lane = lane_id();
     const float l_tot = pair_sum(l_run);                 // a head spans lanes l and l ^ 32
     const int h_own = 32 * c.wave + (lane & 31);
     // (the caller has passed a barrier after every wave is done with the tiles)
@@ -976,13 +982,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(const void* kv, const void* 
     // case for realistic attention; the benchmark times a forced case).
     int* any_beaten = reinterpret_cast<int*>(lds + kAttnTilesLds) + kMaxSlotsPerSplit + 4;
     const bool wave_beaten = __builtin_amdgcn_ballot_w64(beaten) != 0;   // every lane takes part
-    if ((threadIdx.x & 63) == 0) any_beaten[c.wave] = wave_beaten;
+    if (lane_id() == 0) any_beaten[c.wave] = wave_beaten;
     barrier_lds();                       // also: every wave is done with the tiles
     if (any_beaten[0] | any_beaten[1] | any_beaten[2] | any_beaten[3]) {
         attn_pass<true, kRowMajor>(c, m_ref, acc, l_run, beaten, true);
         barrier_lds();                   // every wave is done with the tiles
         attn_pass<false, kRowMajor>(c, m_ref, acc, l_run, beaten, true);
-        if (threadIdx.x == 0) atomicAdd(a.stats, 1);
+        if (c.wave == 0 && lane_id() == 0) atomicAdd(a.stats, 1);
         barrier_lds();                   // every wave is done with the tiles
     }
     attn_finish(c, acc, m_ref, l_run);
