@@ -190,6 +190,15 @@ def test_split_counts(mla, B, k, n_split):
     check_decode(mla, DecodeConfig(40 + n_split, f"splits{n_split}", B=B, T=900, k=k, dtype="bf16"),
                  rows=[0, 1, B // 2, B - 1])
 
+def test_many_splits_ragged_chunk_all_rows(mla):
+    # 20 rows x 2048 slots: thirteen splits of 160 slots, the last one of 128.
+    # Past eight splits the merge takes its many-splits form, and 13 leaves a
+    # last chunk of one split (three clamped loads with weight 0).
+    B, k = 20, 2048
+    assert mla.decode_workspace_size(B, 4096, k, torch.bfloat16) == _bf16_decode_workspace(B, k, 13)
+    check_decode(mla, DecodeConfig(46, "splits13", B=B, T=4096, k=k, dtype="bf16"))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_single_selected_row(mla, dtype):
     check_decode(mla, DecodeConfig(14, "k1", B=2, T=50, k=1, dtype=dtype))
